@@ -1,0 +1,216 @@
+"""Python binding of libextattn.so (argument marshalling only).
+
+Every step of the computation runs in the HIP library; this module checks
+tensor shapes and dtypes, pulls raw device pointers and the current stream
+from PyTorch, and maps status codes to exceptions. If the library has not been
+built it raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libextattn.so")
+
+EXTATTN_OK, EXTATTN_EINVAL, EXTATTN_ENOSPC, EXTATTN_EUNSUPPORTED, EXTATTN_EHIP = 0, -1, -2, -3, -4
+EXTATTN_BF16, EXTATTN_F32 = 0, 1
+BLOCK_SIZE = 16
+
+_lib = None
+
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+_c_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libextattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m chunked_prefill_attention_extend_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.extattn_last_error.restype = ctypes.c_char_p
+    lib.extattn_last_error.argtypes = []
+    lib.extattn_chunk_plan.restype = ctypes.c_int
+    lib.extattn_chunk_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_double, _c_i64p, _c_i64p,
+                                       _c_i64p, _c_i64p, _c_i64p, ctypes.c_int64]
+    lib.extattn_workspace_bytes.restype = ctypes.c_int
+    lib.extattn_workspace_bytes.argtypes = [ctypes.c_int32, _c_i32p, _c_i32p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.extattn_kv_append_workspace_bytes.restype = ctypes.c_size_t
+    lib.extattn_kv_append_workspace_bytes.argtypes = [ctypes.c_int32]
+    lib.extattn_kv_append.restype = ctypes.c_int
+    lib.extattn_kv_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, _c_i32p, _c_i32p,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.extattn_extend_attention.restype = ctypes.c_int
+    lib.extattn_extend_attention.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int32, ctypes.c_int64, _c_i32p, _c_i32p, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc == EXTATTN_OK:
+        return
+    msg = load_library().extattn_last_error().decode(errors="replace")
+    if rc == EXTATTN_EHIP:
+        raise RuntimeError(f"extattn HIP failure: {msg}")
+    kind = {EXTATTN_EINVAL: "invalid argument", EXTATTN_ENOSPC: "insufficient space",
+            EXTATTN_EUNSUPPORTED: "unsupported"}.get(rc, f"status {rc}")
+    raise ValueError(f"extattn {kind}: {msg}")
+
+
+def _host_i32(x: Sequence[int]) -> np.ndarray:
+    if hasattr(x, "detach"):
+        if x.is_cuda:
+            raise ValueError("prefix_lens / extend_lens must be host (CPU) values")
+        x = x.detach().numpy()
+    arr = np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+    if arr.ndim != 1:
+        raise ValueError("length arrays must be one-dimensional")
+    if arr.size and (arr.min() < -2**31 or arr.max() > 2**31 - 1):
+        raise ValueError("lengths must fit int32")
+    return np.ascontiguousarray(arr.astype(np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_c_i32p)
+
+
+def chunk_plan(n_tokens: int, chunk_size: int, hit_rate: float = 0.0) -> dict:
+    """Chunk plan of one prompt: ``{"cached", "effective", "chunks": [(P_t, E_t), ...]}``."""
+    lib = load_library()
+    cached, eff, k = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = lib.extattn_chunk_plan(int(n_tokens), int(chunk_size), float(hit_rate), ctypes.byref(cached),
+                                ctypes.byref(eff), ctypes.byref(k), None, None, 0)
+    if rc != EXTATTN_ENOSPC and rc != EXTATTN_OK:
+        _check(rc)
+    n = k.value
+    p = np.zeros(max(n, 1), np.int64)
+    e = np.zeros(max(n, 1), np.int64)
+    _check(lib.extattn_chunk_plan(int(n_tokens), int(chunk_size), float(hit_rate), ctypes.byref(cached),
+                                  ctypes.byref(eff), ctypes.byref(k), p.ctypes.data_as(_c_i64p),
+                                  e.ctypes.data_as(_c_i64p), n))
+    return {"cached": cached.value, "effective": eff.value,
+            "chunks": [(int(p[t]), int(e[t])) for t in range(n)]}
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return EXTATTN_BF16
+    if t.dtype == torch.float32:
+        return EXTATTN_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def workspace_bytes(prefix_lens, extend_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                    dtype_code: int) -> int:
+    lib = load_library()
+    p, e = _host_i32(prefix_lens), _host_i32(extend_lens)
+    if p.shape != e.shape:
+        raise ValueError("prefix_lens and extend_lens differ in length")
+    out = ctypes.c_size_t()
+    _check(lib.extattn_workspace_bytes(len(p), _ptr(p), _ptr(e), num_q_heads, num_kv_heads, head_dim,
+                                       dtype_code, ctypes.byref(out)))
+    return out.value
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _check_cache(k_cache, v_cache, block_table):
+    import torch
+    if k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("k_cache must be [num_blocks, Hkv, block, D] and v_cache [num_blocks, Hkv, D, block]")
+    nb, hkv, bs, d = k_cache.shape
+    if tuple(v_cache.shape) != (nb, hkv, d, bs):
+        raise ValueError("v_cache must be [num_blocks, Hkv, D, block] (slot-minor)")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [num_seqs, max_blocks] tensor")
+    if not (k_cache.is_cuda and v_cache.is_cuda and block_table.is_cuda):
+        raise ValueError("caches and block_table must be device tensors")
+    return nb, hkv, bs, d
+
+
+def _workspace(nbytes: int, device, workspace):
+    import torch
+    if workspace is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace too small")
+    return workspace
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, block_table, prefix_lens, extend_lens,
+              workspace=None, stream=None) -> None:
+    """Write each request's new K/V rows ``[sum(E), Hkv, D]`` into the paged cache."""
+    lib = load_library()
+    nb, hkv, bs, d = _check_cache(k_cache, v_cache, block_table)
+    p, e = _host_i32(prefix_lens), _host_i32(extend_lens)
+    if p.shape != e.shape or len(p) != block_table.shape[0]:
+        raise ValueError("length arrays must have one entry per block_table row")
+    total = int(e.sum())
+    for t in (k_new, v_new):
+        if tuple(t.shape) != (total, hkv, d) or t.dtype != k_cache.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("k_new / v_new must be contiguous device tensors [sum(E), Hkv, D] of the cache dtype")
+    need = lib.extattn_kv_append_workspace_bytes(len(p))
+    ws = _workspace(need, k_cache.device, workspace)
+    _check(lib.extattn_kv_append(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                 block_table.data_ptr(), block_table.shape[1], nb, _ptr(p), _ptr(e), len(p),
+                                 hkv, d, bs, _dtype_code(k_cache), ws.data_ptr(),
+                                 ws.numel() * ws.element_size(), _stream_handle(stream)))
+
+
+def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale: float, out,
+                     lse=None, workspace=None, stream=None):
+    """Chunked-prefill extend attention over the paged cache.
+
+    q, out: device ``[sum(E), Hq, D]``; lse: device float32 ``[sum(E), Hq]`` or None;
+    prefix_lens / extend_lens: host, one entry per block_table row.
+    Returns ``out``.
+    """
+    import torch
+    lib = load_library()
+    nb, hkv, bs, d = _check_cache(k_cache, v_cache, block_table)
+    p, e = _host_i32(prefix_lens), _host_i32(extend_lens)
+    if p.shape != e.shape or len(p) != block_table.shape[0]:
+        raise ValueError("length arrays must have one entry per block_table row")
+    total = int(e.sum())
+    if q.dim() != 3 or q.shape[0] != total or q.shape[2] != d:
+        raise ValueError("q must be [sum(E), Hq, D]")
+    hq = q.shape[1]
+    if q.dtype != k_cache.dtype or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError("q must be a contiguous device tensor of the cache dtype")
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must match q")
+    if lse is not None and (tuple(lse.shape) != (total, hq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [sum(E), Hq] tensor")
+    code = _dtype_code(q)
+    need = workspace_bytes(p, e, hq, hkv, d, code)
+    ws = _workspace(need, q.device, workspace)
+    _check(lib.extattn_extend_attention(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                        block_table.data_ptr(), block_table.shape[1], nb, _ptr(p), _ptr(e),
+                                        len(p), hq, hkv, d, bs, float(scale), code, out.data_ptr(),
+                                        lse.data_ptr() if lse is not None else None, ws.data_ptr(),
+                                        ws.numel() * ws.element_size(), _stream_handle(stream)))
+    return out

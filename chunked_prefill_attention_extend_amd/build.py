@@ -1,0 +1,78 @@
+"""Build libextattn.so in-tree with hipcc for gfx950.
+
+Device code (.hip) is compiled with hipcc; host-only C++ (.cpp) with g++
+against the HIP runtime headers. Packed fp32 instructions are disabled for all
+device code. The library is written next to this file.
+
+    python -m chunked_prefill_attention_extend_amd.build
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libextattn.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+CXX_FLAGS = [
+    "-O2", "-fPIC", "-std=c++17", "-D__HIP_PLATFORM_AMD__",
+    "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"),
+    "-Wall", "-Wextra",
+]
+
+
+def _run(cmd: list[str]) -> None:
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+
+
+def sources() -> tuple[list[str], list[str]]:
+    files = sorted(os.listdir(CSRC))
+    hip = [os.path.join(CSRC, f) for f in files if f.endswith(".hip")]
+    cpp = [os.path.join(CSRC, f) for f in files if f.endswith(".cpp")]
+    return hip, cpp
+
+
+def build(verbose: bool = False, extra_hip_flags: list[str] | None = None) -> str:
+    hip, cpp = sources()
+    tmp = tempfile.mkdtemp(prefix="extattn_build_")
+    try:
+        jobs = []
+        for src in hip:
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            jobs.append(([HIPCC, *HIP_FLAGS, *(extra_hip_flags or []), "-c", src, "-o", obj], obj))
+        for src in cpp:
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            jobs.append((["g++", *CXX_FLAGS, "-c", src, "-o", obj], obj))
+        with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+            list(ex.map(lambda j: _run(j[0]), jobs))
+        out_tmp = os.path.join(tmp, "libextattn.so")
+        _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[o for _, o in jobs], "-o", out_tmp])
+        shutil.move(out_tmp, LIB + ".tmp")
+        os.replace(LIB + ".tmp", LIB)
+        if verbose:
+            print(f"built {LIB}")
+        return LIB
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,285 @@
+// The C ABI: argument checks, metadata upload, kernel launches.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/extattn.h"
+#include "internal.hpp"
+
+namespace extattn {
+int chunk_plan_impl(int64_t n_tokens, int64_t chunk_size, double hit_rate, int64_t* cached,
+                    int64_t* effective, int64_t* n_chunks, int64_t* prefix_lens, int64_t* extend_lens,
+                    int64_t capacity, const char** why);
+}
+
+using namespace extattn;
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const std::string& msg) {
+  g_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), "%s: %s", what, hipGetErrorString(e));
+  g_error = buf;
+  return EXTATTN_EHIP;
+}
+
+// Pinned host staging for the metadata copied into the caller's workspace.
+// A small ring of buffers per device; a buffer is reused only after the copy
+// that last read it has completed (tracked with an event).
+struct StagingSlot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+
+constexpr int kRing = 8;
+constexpr int kMaxDevices = 64;
+
+struct DeviceStaging {
+  StagingSlot slots[kRing];
+  int next = 0;
+};
+
+std::mutex g_staging_mu;
+DeviceStaging g_staging[kMaxDevices];
+
+int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(EXTATTN_EHIP, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_staging_mu);
+  DeviceStaging& ds = g_staging[dev];
+  StagingSlot& s = ds.slots[ds.next];
+  ds.next = (ds.next + 1) % kRing;
+  if (s.pending) {
+    e = hipEventSynchronize(s.done);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (staging)");
+    s.pending = false;
+  }
+  if (!s.done) {
+    e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate (staging)");
+  }
+  if (s.cap < bytes) {
+    if (s.host) hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    size_t cap = 1 << 16;
+    while (cap < bytes) cap *= 2;
+    e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc (staging)");
+    s.cap = cap;
+  }
+  std::memcpy(s.host, src, bytes);
+  e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (metadata)");
+  e = hipEventRecord(s.done, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord (staging)");
+  s.pending = true;
+  return EXTATTN_OK;
+}
+
+int check_common(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
+                 int32_t head_dim, int32_t dtype, bool extend_min_one) {
+  if (num_seqs < 1) return fail(EXTATTN_EINVAL, "num_seqs must be >= 1");
+  if (!prefix || !extend) return fail(EXTATTN_EINVAL, "prefix_lens and extend_lens must be host arrays");
+  if (hkv < 1 || hq < 1) return fail(EXTATTN_EINVAL, "head counts must be >= 1");
+  if (hq % hkv != 0) return fail(EXTATTN_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
+  if (head_dim != 64 && head_dim != 128) return fail(EXTATTN_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (dtype != EXTATTN_BF16 && dtype != EXTATTN_F32) return fail(EXTATTN_EUNSUPPORTED, "unknown dtype");
+  int64_t total = 0;
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    if (prefix[r] < 0) return fail(EXTATTN_EINVAL, "prefix_lens[" + std::to_string(r) + "] < 0");
+    if (extend[r] < (extend_min_one ? 1 : 0))
+      return fail(EXTATTN_EINVAL, "extend_lens[" + std::to_string(r) + "] out of range");
+    if (int64_t(prefix[r]) + extend[r] > INT32_MAX)
+      return fail(EXTATTN_EINVAL, "prefix + extend exceeds 2^31-1");
+    total += extend[r];
+  }
+  if (total > INT32_MAX) return fail(EXTATTN_EINVAL, "sum of extend_lens exceeds 2^31-1");
+  return EXTATTN_OK;
+}
+
+int check_blocks(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t max_blocks,
+                 int64_t num_blocks, int32_t block_size) {
+  if (block_size != kBlockSize) return fail(EXTATTN_EUNSUPPORTED, "block_size must be 16");
+  if (max_blocks < 1) return fail(EXTATTN_EINVAL, "max_blocks must be >= 1");
+  if (num_blocks < 1) return fail(EXTATTN_EINVAL, "num_blocks must be >= 1");
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    const int64_t need = (int64_t(prefix[r]) + extend[r] + kBlockSize - 1) / kBlockSize;
+    if (need > max_blocks)
+      return fail(EXTATTN_EINVAL, "request " + std::to_string(r) + " needs more than max_blocks blocks");
+  }
+  return EXTATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* extattn_last_error(void) { return g_error.c_str(); }
+
+int extattn_chunk_plan(int64_t n_tokens, int64_t chunk_size, double hit_rate, int64_t* cached,
+                       int64_t* effective, int64_t* n_chunks, int64_t* prefix_lens, int64_t* extend_lens,
+                       int64_t capacity) {
+  const char* why = "";
+  const int rc = chunk_plan_impl(n_tokens, chunk_size, hit_rate, cached, effective, n_chunks, prefix_lens,
+                                 extend_lens, capacity, &why);
+  if (rc != EXTATTN_OK) return fail(rc, why);
+  g_error.clear();
+  return EXTATTN_OK;
+}
+
+int extattn_workspace_bytes(int32_t num_seqs, const int32_t* prefix_lens, const int32_t* extend_lens,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                            size_t* bytes) {
+  if (!bytes) return fail(EXTATTN_EINVAL, "bytes must not be null");
+  int rc = check_common(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, true);
+  if (rc != EXTATTN_OK) return rc;
+  Plan plan;
+  rc = build_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, plan);
+  if (rc != EXTATTN_OK) return fail(rc, "planning failed");
+  *bytes = plan.bytes;
+  g_error.clear();
+  return EXTATTN_OK;
+}
+
+size_t extattn_kv_append_workspace_bytes(int32_t num_seqs) {
+  if (num_seqs < 0) num_seqs = 0;
+  return kHeaderBytes + sizeof(SeqInfo) * size_t(num_seqs);
+}
+
+int extattn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int32_t* block_table, int32_t max_blocks, int64_t num_blocks,
+                      const int32_t* prefix_lens, const int32_t* extend_lens, int32_t num_seqs,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(num_seqs, prefix_lens, extend_lens, num_kv_heads, num_kv_heads, head_dim, dtype, false);
+  if (rc != EXTATTN_OK) return rc;
+  rc = check_blocks(num_seqs, prefix_lens, extend_lens, max_blocks, num_blocks, block_size);
+  if (rc != EXTATTN_OK) return rc;
+  if (!k_cache || !v_cache || !block_table || !workspace)
+    return fail(EXTATTN_EINVAL, "null device pointer");
+  const size_t need = extattn_kv_append_workspace_bytes(num_seqs);
+  if (workspace_bytes < need) return fail(EXTATTN_ENOSPC, "workspace too small for kv_append");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(EXTATTN_EINVAL, "workspace must be 256-byte aligned");
+  std::vector<unsigned char> blob(need, 0);
+  int64_t q_off = 0;
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    SeqInfo s{int32_t(q_off), prefix_lens[r], extend_lens[r], 0};
+    std::memcpy(blob.data() + kHeaderBytes + sizeof(SeqInfo) * r, &s, sizeof(s));
+    q_off += extend_lens[r];
+  }
+  if (q_off == 0) { g_error.clear(); return EXTATTN_OK; }
+  if (!k_new || !v_new) return fail(EXTATTN_EINVAL, "null k_new / v_new");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  rc = upload(blob.data(), need, workspace, st);
+  if (rc != EXTATTN_OK) return rc;
+  KvArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seqs = reinterpret_cast<const SeqInfo*>(static_cast<unsigned char*>(workspace) + kHeaderBytes);
+  a.err = static_cast<int32_t*>(workspace);
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks;
+  a.num_seqs = num_seqs;
+  a.hkv = num_kv_heads;
+  a.head_dim = head_dim;
+  a.total_tokens = int32_t(q_off);
+  hipError_t e = launch_kv_append(a, dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+  g_error.clear();
+  return EXTATTN_OK;
+}
+
+int extattn_extend_attention(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, int32_t max_blocks, int64_t num_blocks,
+                             const int32_t* prefix_lens, const int32_t* extend_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, float scale, int32_t dtype, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, true);
+  if (rc != EXTATTN_OK) return rc;
+  rc = check_blocks(num_seqs, prefix_lens, extend_lens, max_blocks, num_blocks, block_size);
+  if (rc != EXTATTN_OK) return rc;
+  if (!q || !k_cache || !v_cache || !block_table || !out || !workspace)
+    return fail(EXTATTN_EINVAL, "null device pointer");
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(EXTATTN_EINVAL, "scale must be finite and > 0");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(EXTATTN_EINVAL, "workspace must be 256-byte aligned");
+  Plan plan;
+  rc = build_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, plan);
+  if (rc != EXTATTN_OK) return fail(rc, "planning failed");
+  if (workspace_bytes < plan.bytes) return fail(EXTATTN_ENOSPC, "workspace too small");
+
+  std::vector<unsigned char> blob(plan.upload_bytes, 0);
+  std::memcpy(blob.data() + plan.off_seqs, plan.seqs.data(), sizeof(SeqInfo) * plan.seqs.size());
+  if (!plan.items.empty())
+    std::memcpy(blob.data() + plan.off_items, plan.items.data(), sizeof(WorkItem) * plan.items.size());
+  if (!plan.tasks.empty())
+    std::memcpy(blob.data() + plan.off_tasks, plan.tasks.data(), sizeof(CombineTask) * plan.tasks.size());
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  rc = upload(blob.data(), blob.size(), workspace, st);
+  if (rc != EXTATTN_OK) return rc;
+
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.out = out;
+  a.lse = lse;
+  a.seqs = reinterpret_cast<const SeqInfo*>(ws + plan.off_seqs);
+  a.items = reinterpret_cast<const WorkItem*>(ws + plan.off_items);
+  a.tasks = reinterpret_cast<const CombineTask*>(ws + plan.off_tasks);
+  a.slots = reinterpret_cast<float*>(ws + plan.off_slots);
+  a.err = reinterpret_cast<int32_t*>(ws);
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks;
+  a.num_seqs = num_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.total_rows = int32_t(plan.total_rows);
+  a.n_items = int32_t(plan.items.size());
+  a.n_tasks = int32_t(plan.tasks.size());
+
+  hipError_t e;
+  if (dtype == EXTATTN_F32) {
+    e = launch_attn_f32(a, st);
+    if (e != hipSuccess) return hip_fail(e, "fp32 attention launch");
+  } else {
+    if (a.n_items > 0) {
+      e = launch_attn_bf16(a, st);
+      if (e != hipSuccess) return hip_fail(e, "bf16 attention launch");
+    }
+    if (a.n_tasks > 0) {
+      e = launch_combine(a, dtype, st);
+      if (e != hipSuccess) return hip_fail(e, "combine launch");
+    }
+  }
+  g_error.clear();
+  return EXTATTN_OK;
+}
+
+}  // extern "C"

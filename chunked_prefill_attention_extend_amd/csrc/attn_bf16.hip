@@ -1,0 +1,385 @@
+// bf16 extend attention on the CDNA4 matrix cores (gfx950).
+//
+// What is computed (zdszero "Chunked Prefill" notes, section "prefill as
+// several resumable extends"): query token i of a chunk at global position
+// P + i takes the softmax over keys 0 .. P+i of scale * q.k_j and applies it
+// to v_j. Keys below P are the rectangle (never masked), keys P .. P+i the
+// triangle (the causal diagonal); both are swept by one running (m, l)
+// online-softmax state, which is the page's merge rule applied tile by tile.
+// Split key ranges end in a partial (o, lse) that the combine kernel merges
+// with the same rule.
+//
+// Layout of the work (one workgroup = 4 wave64):
+//  * Rows are (position, head-in-group) pairs of one (request, KV head): the
+//    whole GQA group shares each K/V tile.
+//  * Chunk items: 128 rows, the 4 waves hold 32 rows each; K/V tiles of 64
+//    keys are copied from the paged cache into LDS once per workgroup
+//    (double buffered, one barrier per tile) and read by all 4 waves.
+//  * Split items (<= 32 rows: decode rows, short verify rows): every wave
+//    reads its own part of the key range straight from HBM into MFMA operand
+//    registers; no LDS.
+//
+// The contraction runs transposed: S^T = K Q^T and O^T = V^T P^T on
+// v_mfma_f32_32x32x16_bf16. A lane then owns one query row (column l % 32 of
+// every accumulator), so the row max / row sum stay in-lane except for one
+// exchange with lane l ^ 32, and the P^T operand of the second product is the
+// first product's accumulator converted to bf16 in place. The key order inside
+// a 32-key block is permuted (bits 2 and 3 of the row index swapped) so that
+// each lane's 8 P^T values cover 8 consecutive keys, which makes the V^T
+// operand one 16-byte read of the slot-minor V cache layout.
+#include "device_common.hpp"
+
+namespace extattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+__device__ inline uint32_t pack2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Key (within a 32-key block) that MFMA row m of the S^T product holds.
+__device__ inline int key_of_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Key (within a 32-key block) of accumulator element i in lane half `hi`.
+__device__ inline int key_of_elem(int i, int hi) { return ((i >> 3) << 4) + (hi << 3) + (i & 7); }
+
+__device__ inline u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// Zero the bf16 values of a 16-byte V piece whose keys k0 .. k0+7 reach kv_len.
+__device__ inline u32x4 clip_keys(u32x4 v, int k0, int kv_len) {
+  if (k0 + 8 <= kv_len) return v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = (k0 + 2 * w < kv_len) ? 0x0000ffffu : 0u;
+    const uint32_t hi = (k0 + 2 * w + 1 < kv_len) ? 0xffff0000u : 0u;
+    v[w] &= (lo | hi);
+  }
+  return v;
+}
+
+// One online-softmax step over NKB 32-key blocks of raw scores.
+// m is kept in log2 units of the scaled scores; l is this lane's share of the
+// row sum (the two lanes of a row add theirs at the end).
+template <int NKB, int DB>
+__device__ inline void softmax_step(f32x16 (&s)[NKB], f32x16 (&o)[DB], float& m, float& l, float scale_log2,
+                                    u32x4 (&pf)[NKB][2]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mnew = fmaxf(m, mx * scale_log2);
+  if (mnew > m) {
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 when m is -inf
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    l *= alpha;
+    m = mnew;
+  }
+  const float msafe = (m == -INFINITY) ? 0.f : m;
+  float ls = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * v + 2 * w], scale_log2, -msafe));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * v + 2 * w + 1], scale_log2, -msafe));
+        ls += p0 + p1;
+        pf[kb][v][w] = pack2(p0, p1);
+      }
+  l += ls;
+}
+
+// Write a finished row: either the final output (bf16) and lse, or a partial
+// slot (fp32 o normalised, natural-log lse) for the combine kernel.
+template <int D>
+__device__ inline void write_row(const AttnArgs& a, const f32x16 (&o)[D / 32], float m, float l, bool valid,
+                                 int hi, int64_t orow, int slot, int rloc) {
+  constexpr int DB = D / 32;
+  const float lt = l + __shfl_xor(l, 32);
+  if (!valid) return;
+  if (slot < 0) {
+    const float inv = 1.f / lt;
+    uint16_t* op = static_cast<uint16_t*>(a.out) + orow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int d = db * 32 + u * 8 + hi * 4;
+        u32x2 pk = {pack2(o[db][4 * u] * inv, o[db][4 * u + 1] * inv),
+                    pack2(o[db][4 * u + 2] * inv, o[db][4 * u + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + d) = pk;
+      }
+    if (hi == 0 && a.lse) a.lse[orow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+  } else {
+    float* sl = a.slots + size_t(slot) * slot_floats(D);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int d = db * 32 + u * 8 + hi * 4;
+        float4 v = {o[db][4 * u] * inv, o[db][4 * u + 1] * inv, o[db][4 * u + 2] * inv, o[db][4 * u + 3] * inv};
+        *reinterpret_cast<float4*>(sl + rloc * D + d) = v;
+      }
+    if (hi == 0) sl[kRowsPerWave * D + rloc] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk items: 128 rows, LDS-shared K/V tiles of 64 keys.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char* smem) {
+  constexpr int NC = D / 8;                       // 16-byte pieces per K row
+  constexpr int KS = D / 16;                      // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;                      // 32-feature blocks of O^T
+  constexpr int KT_BYTES = kKeyTile * D * 2;      // one K tile (= one V tile)
+  constexpr int STAGE = 2 * KT_BYTES;
+  constexpr int BLK_PIECES = kBlockSize * NC;     // 16-byte pieces per (block, head)
+  constexpr int LOADS = kKeyTile * NC / kThreads; // pieces per thread per tile
+  constexpr int VROW = kKeyTile * 2;              // bytes per V^T row in LDS
+  static_assert(LOADS >= 1, "tile too small for the workgroup");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const SeqInfo si = a.seqs[it.seq];
+  const int G = a.group, g = it.kv_head;
+  const int kv_len = si.prefix + si.extend;
+  const int rloc = wave * kRowsPerWave + l32;
+  const bool valid = rloc < it.nrows;
+  const int rho = it.row0 + rloc;
+  const int pos = valid ? rho / G : 0;
+  const int hh = valid ? rho - pos * G : 0;
+  const int64_t orow = int64_t(si.q_off + pos) * a.hq + g * G + hh;
+  const int lim = valid ? min(si.prefix + pos, it.key_end - 1) : -1;
+  const int lim_min = min(si.prefix + it.row0 / G, it.key_end - 1);
+
+  u32x4 qf[KS];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + orow * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = valid ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : zero4();
+  }
+
+  const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
+  const int nblk = (kv_len + kBlockSize - 1) / kBlockSize;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+
+  u32x4 kreg[LOADS], vreg[LOADS];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int x = 0; x < LOADS; ++x) {
+      const int i = tid + kThreads * x;
+      const int b = i / BLK_PIECES, off = i % BLK_PIECES;
+      const int lb = j * (kKeyTile / kBlockSize) + b;
+      const int32_t phys = lb < nblk ? bt[lb] : -1;
+      const bool ok = block_ok(phys, a.num_blocks);
+      if (lb < nblk && !ok && off == 0) atomicAdd(a.err, 1);
+      const int64_t base = (int64_t(phys) * a.hkv + g) * (kBlockSize * D) + off * 8;
+      kreg[x] = ok ? *reinterpret_cast<const u32x4*>(kc + base) : zero4();
+      const u32x4 vv = ok ? *reinterpret_cast<const u32x4*>(vc + base) : zero4();
+      vreg[x] = clip_keys(vv, lb * kBlockSize + (off & 1) * 8, kv_len);
+    }
+  };
+  auto store_tile = [&](int stage) {
+    unsigned char* ks_ = smem + stage * STAGE;
+    unsigned char* vs_ = ks_ + KT_BYTES;
+#pragma unroll
+    for (int x = 0; x < LOADS; ++x) {
+      const int i = tid + kThreads * x;
+      const int b = i / BLK_PIECES, off = i % BLK_PIECES;
+      const int kr = b * kBlockSize + off / NC, kp = off % NC;
+      *reinterpret_cast<u32x4*>(ks_ + kr * (D * 2) + ((kp ^ (kr % NC)) << 4)) = kreg[x];
+      const int d = off >> 1, vp = b * 2 + (off & 1);
+      *reinterpret_cast<u32x4*>(vs_ + d * VROW + ((vp ^ ((d >> 1) & 7)) << 4)) = vreg[x];
+    }
+  };
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  auto compute = [&](int stage, int j) {
+    const unsigned char* ks_ = smem + stage * STAGE;
+    const unsigned char* vs_ = ks_ + KT_BYTES;
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const int kr = kb * 32 + key_of_row(l32);
+      const unsigned char* krow = ks_ + kr * (D * 2);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + (((ks * 2 + hi) ^ (kr % NC)) << 4));
+        s[kb] = mfma32(kf, qf[ks], s[kb]);
+      }
+    }
+    const int kt = j * kKeyTile;
+    if (kt + kKeyTile - 1 > lim_min) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kt + kb * 32 + key_of_elem(i, hi) > lim) s[kb][i] = -INFINITY;
+    }
+    u32x4 pf[2][2];
+    softmax_step<2, DB>(s, o, m, l, a.scale_log2, pf);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = db * 32 + l32;
+      const unsigned char* vrow = vs_ + d * VROW;
+      const int sw = (d >> 1) & 7;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const int vp = kb * 4 + v * 2 + hi;
+          const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + ((vp ^ sw) << 4));
+          o[db] = mfma32(vf, pf[kb][v], o[db]);
+        }
+    }
+  };
+
+  const int t0 = it.key_begin / kKeyTile;
+  const int t1 = (it.key_end + kKeyTile - 1) / kKeyTile;
+  if (t0 < t1) {
+    load_tile(t0);
+    store_tile(0);
+    if (t0 + 1 < t1) load_tile(t0 + 1);
+    __syncthreads();
+    for (int j = t0; j < t1; ++j) {
+      const int stage = (j - t0) & 1;
+      compute(stage, j);
+      if (j + 1 < t1) {
+        store_tile(stage ^ 1);
+        if (j + 2 < t1) load_tile(j + 2);
+      }
+      __syncthreads();
+    }
+  }
+  write_row<D>(a, o, m, l, valid, hi, orow, it.slot < 0 ? -1 : it.slot + wave, rloc);
+}
+
+// ---------------------------------------------------------------------------
+// Split items: <= 32 rows, each wave streams its own keys from HBM.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ void split_item(const AttnArgs& a, const WorkItem& it) {
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const SeqInfo si = a.seqs[it.seq];
+  const int G = a.group, g = it.kv_head;
+  const int kv_len = si.prefix + si.extend;
+  const bool valid = l32 < it.nrows;
+  const int pos = valid ? l32 / G : 0;
+  const int hh = valid ? l32 - pos * G : 0;
+  const int64_t orow = int64_t(si.q_off + pos) * a.hq + g * G + hh;
+  const int lim = valid ? min(si.prefix + pos, it.key_end - 1) : -1;
+
+  u32x4 qf[KS];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + orow * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = valid ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : zero4();
+  }
+  const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
+  const int nblk = (kv_len + kBlockSize - 1) / kBlockSize;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  const int nt = (it.key_end - it.key_begin + kSplitTile - 1) / kSplitTile;
+  const int tw0 = wave * nt / 4, tw1 = (wave + 1) * nt / 4;
+  const int krow = key_of_row(l32);
+  for (int jj = tw0; jj < tw1; ++jj) {
+    const int kt = it.key_begin + jj * kSplitTile;
+    const int lb0 = kt / kBlockSize;
+    const int32_t p0 = lb0 < nblk ? bt[lb0] : -1;
+    const int32_t p1 = lb0 + 1 < nblk ? bt[lb0 + 1] : -1;
+    const bool ok0 = block_ok(p0, a.num_blocks), ok1 = block_ok(p1, a.num_blocks);
+    if (wave == 0 && lane == 0) {
+      if (lb0 < nblk && !ok0) atomicAdd(a.err, 1);
+      if (lb0 + 1 < nblk && !ok1) atomicAdd(a.err, 1);
+    }
+    // K operand: this lane's MFMA row holds key kt + krow.
+    const int key = kt + krow;
+    const int32_t pk = krow < kBlockSize ? p0 : p1;
+    const bool okk = (krow < kBlockSize ? ok0 : ok1) && key < kv_len;
+    const uint16_t* kp = kc + ((int64_t(pk) * a.hkv + g) * kBlockSize + (key % kBlockSize)) * D + hi * 8;
+    u32x4 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = okk ? *reinterpret_cast<const u32x4*>(kp + ks * 16) : zero4();
+    // V^T operand: feature db*32 + l32, keys kt + 16 v + 8 hi .. +8.
+    u32x4 vf[DB][2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int32_t pv = v ? p1 : p0;
+      const bool okv = v ? ok1 : ok0;
+      const uint16_t* vp = vc + (int64_t(pv) * a.hkv + g) * (kBlockSize * D) + hi * 8;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x4 raw = okv ? *reinterpret_cast<const u32x4*>(vp + (db * 32 + l32) * kBlockSize) : zero4();
+        vf[db][v] = clip_keys(raw, kt + 16 * v + 8 * hi, kv_len);
+      }
+    }
+    f32x16 s[1];
+    s[0] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s[0] = mfma32(kf[ks], qf[ks], s[0]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (kt + key_of_elem(i, hi) > lim) s[0][i] = -INFINITY;
+    u32x4 pf[1][2];
+    softmax_step<1, DB>(s, o, m, l, a.scale_log2, pf);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) o[db] = mfma32(vf[db][v], pf[0][v], o[db]);
+  }
+  write_row<D>(a, o, m, l, valid, hi, orow, it.slot + wave, l32);
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
+void attn_bf16_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * kKeyTile * D * 2];
+  const WorkItem it = a.items[blockIdx.x];
+  if (it.kind == kItemChunk)
+    chunk_item<D>(a, it, smem);
+  else
+    split_item<D>(a, it);
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {
+  if (a.n_items <= 0) return hipSuccess;
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(unsigned(a.n_items)), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(unsigned(a.n_items)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace extattn

@@ -1,0 +1,126 @@
+// Internal definitions shared by the host planner, the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+namespace extattn {
+
+constexpr int kBlockSize = 16;    // tokens per paged-cache block
+constexpr int kThreads = 256;     // 4 wave64 per workgroup
+constexpr int kRowsPerWave = 32;  // query rows per wave (one 32x32 MFMA column block)
+constexpr int kRowsPerTile = 128; // chunk path: 4 waves x 32 rows share each K/V tile
+constexpr int kKeyTile = 64;      // chunk path: keys per LDS K/V tile
+constexpr int kSplitTile = 32;    // split path: keys per register K/V tile
+constexpr int kSplitKeys = 1024;  // split path: keys per workgroup (4 waves)
+
+// Per-request metadata copied to the workspace.
+struct SeqInfo {
+  int32_t q_off;   // first query row of the request in q / out
+  int32_t prefix;  // P: tokens already in the cache before this chunk
+  int32_t extend;  // E: new query tokens
+  int32_t pad;
+};
+
+enum : int32_t {
+  kItemChunk = 0,  // 128 rows of one (request, KV head); 4 waves share LDS K/V tiles
+  kItemSplit = 1,  // <= 32 rows; each of the 4 waves takes its own part of the key range
+};
+
+// One workgroup's work. Rows are flattened per (request, KV head) as
+// row = pos * group + head_in_group, pos in [0, E), head_in_group in [0, group).
+struct WorkItem {
+  int32_t kind;
+  int32_t seq;
+  int32_t kv_head;
+  int32_t row0;       // first flattened row
+  int32_t nrows;      // rows in this item (<= 128 chunk, <= 32 split)
+  int32_t key_begin;  // keys [key_begin, key_end); key_begin is a multiple of kKeyTile
+  int32_t key_end;
+  int32_t slot;       // < 0: write out/lse directly; else first partial slot (one per wave)
+};
+
+// Merge of partial results for <= 32 rows of one (request, KV head).
+struct CombineTask {
+  int32_t seq;
+  int32_t kv_head;
+  int32_t row0;
+  int32_t nrows;
+  int32_t slot0;   // slots slot0 + i * stride, i in [0, nslots)
+  int32_t nslots;
+  int32_t stride;
+  int32_t pad;
+};
+
+// Partial slot: o (normalised, fp32) [32][D] then lse (natural log) [32].
+inline constexpr size_t slot_floats(int head_dim) { return size_t(kRowsPerWave) * head_dim + kRowsPerWave; }
+
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  void* out;
+  float* lse;
+  const SeqInfo* seqs;
+  const WorkItem* items;
+  const CombineTask* tasks;
+  float* slots;
+  int32_t* err;
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;
+  int32_t head_dim;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+  int32_t total_rows;
+  int32_t n_items;
+  int32_t n_tasks;
+};
+
+struct KvArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const SeqInfo* seqs;
+  int32_t* err;
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t hkv;
+  int32_t head_dim;
+  int32_t total_tokens;
+};
+
+// Host plan of one extend_attention call.
+struct Plan {
+  std::vector<SeqInfo> seqs;
+  std::vector<WorkItem> items;
+  std::vector<CombineTask> tasks;
+  int64_t n_slots = 0;
+  int64_t total_rows = 0;
+  // byte offsets inside the workspace
+  size_t off_seqs = 0, off_items = 0, off_tasks = 0, off_slots = 0, bytes = 0, upload_bytes = 0;
+};
+
+constexpr size_t kHeaderBytes = 256;  // error word + padding
+
+// plan.cpp
+int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
+               int32_t head_dim, int32_t dtype, Plan& plan);
+
+// kernel launchers (one per .hip file)
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_combine(const AttnArgs& a, int32_t dtype, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_kv_append(const KvArgs& a, int32_t dtype, hipStream_t stream);
+
+}  // namespace extattn

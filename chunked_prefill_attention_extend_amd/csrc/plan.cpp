@@ -1,0 +1,119 @@
+// Host-side planning: the chunk plan of one prompt and the work list of one
+// extend-attention launch.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/extattn.h"
+#include "internal.hpp"
+
+namespace extattn {
+
+// Chunk plan (msmodeling chunked-prefill RFC, sections 2.2 and 3.1.3; zdszero
+// notes, section "prefill as several resumable extends"): the cached prefix is
+// floor(N * hit_rate) with one double multiply; the remaining effective tokens
+// are cut into ceil(effective / C) chunks of C tokens, the last one shorter.
+int chunk_plan_impl(int64_t n_tokens, int64_t chunk_size, double hit_rate, int64_t* cached,
+                    int64_t* effective, int64_t* n_chunks, int64_t* prefix_lens, int64_t* extend_lens,
+                    int64_t capacity, const char** why) {
+  if (n_tokens < 1) { *why = "n_tokens must be >= 1"; return EXTATTN_EINVAL; }
+  if (chunk_size < 1) { *why = "chunk_size must be >= 1"; return EXTATTN_EINVAL; }
+  if (!(hit_rate >= 0.0 && hit_rate <= 1.0)) { *why = "hit_rate must lie in [0, 1]"; return EXTATTN_EINVAL; }
+  if (!cached || !effective || !n_chunks) { *why = "null output pointer"; return EXTATTN_EINVAL; }
+  volatile double product = static_cast<double>(n_tokens) * hit_rate;  // one IEEE multiply, no fusion
+  const int64_t c = static_cast<int64_t>(std::floor(product));
+  const int64_t eff = n_tokens - c;
+  if (eff < 1) { *why = "effective length after prefix-cache hits must be >= 1"; return EXTATTN_EINVAL; }
+  const int64_t k = eff / chunk_size + (eff % chunk_size != 0);
+  *cached = c;
+  *effective = eff;
+  *n_chunks = k;
+  if (capacity < k) { *why = "capacity is smaller than the number of chunks"; return EXTATTN_ENOSPC; }
+  if (!prefix_lens || !extend_lens) { *why = "null plan array"; return EXTATTN_EINVAL; }
+  for (int64_t t = 0; t < k; ++t) {
+    const int64_t done = std::min(t * chunk_size, eff);
+    prefix_lens[t] = c + done;
+    extend_lens[t] = std::min(chunk_size, eff - done);
+  }
+  return EXTATTN_OK;
+}
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Work list of one launch. Requests whose E * group rows fit one wave (decode
+// rows, short verify rows) take the split path: the key range is cut into
+// kSplitKeys pieces, each piece into four per-wave parts, and the partial
+// results are merged by the combine kernel. Longer chunks take the chunk path:
+// 128-row tiles over their whole causal key range.
+int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
+               int32_t head_dim, int32_t dtype, Plan& plan) {
+  const int32_t group = hq / hkv;
+  plan.seqs.resize(num_seqs);
+  plan.items.clear();
+  plan.tasks.clear();
+  plan.n_slots = 0;
+  int64_t q_off = 0;
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    plan.seqs[r] = SeqInfo{static_cast<int32_t>(q_off), prefix[r], extend[r], 0};
+    q_off += extend[r];
+  }
+  plan.total_rows = q_off;
+
+  if (dtype == EXTATTN_BF16) {
+    std::vector<WorkItem> chunk_items, split_items;
+    for (int32_t r = 0; r < num_seqs; ++r) {
+      const int64_t rows = int64_t(extend[r]) * group;
+      const int64_t kv_len = int64_t(prefix[r]) + extend[r];
+      if (rows <= kRowsPerWave) {
+        const int64_t nwg = (kv_len + kSplitKeys - 1) / kSplitKeys;
+        for (int32_t g = 0; g < hkv; ++g) {
+          const int64_t slot0 = plan.n_slots;
+          for (int64_t w = 0; w < nwg; ++w) {
+            const int64_t kb = w * kSplitKeys;
+            const int64_t ke = std::min<int64_t>(kv_len, kb + kSplitKeys);
+            split_items.push_back(WorkItem{kItemSplit, r, g, 0, int32_t(rows), int32_t(kb), int32_t(ke),
+                                           int32_t(slot0 + 4 * w)});
+          }
+          plan.tasks.push_back(CombineTask{r, g, 0, int32_t(rows), int32_t(slot0), int32_t(4 * nwg), 1, 0});
+          plan.n_slots += 4 * nwg;
+        }
+      } else {
+        const int64_t ntiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
+        for (int32_t g = 0; g < hkv; ++g) {
+          for (int64_t t = 0; t < ntiles; ++t) {
+            const int64_t row0 = t * kRowsPerTile;
+            const int64_t nrows = std::min<int64_t>(kRowsPerTile, rows - row0);
+            const int64_t pos_max = (row0 + nrows - 1) / group;
+            const int64_t key_end = int64_t(prefix[r]) + pos_max + 1;
+            chunk_items.push_back(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), 0,
+                                           int32_t(key_end), -1});
+          }
+        }
+      }
+    }
+    // Longest chunk tiles first (they set the makespan), then the split work.
+    std::stable_sort(chunk_items.begin(), chunk_items.end(), [](const WorkItem& x, const WorkItem& y) {
+      return int64_t(x.key_end - x.key_begin) * x.nrows > int64_t(y.key_end - y.key_begin) * y.nrows;
+    });
+    std::stable_sort(split_items.begin(), split_items.end(), [](const WorkItem& x, const WorkItem& y) {
+      return (x.key_end - x.key_begin) > (y.key_end - y.key_begin);
+    });
+    plan.items = std::move(chunk_items);
+    plan.items.insert(plan.items.end(), split_items.begin(), split_items.end());
+  }
+
+  size_t off = kHeaderBytes;
+  plan.off_seqs = off;
+  off = align_up(off + sizeof(SeqInfo) * num_seqs, 256);
+  plan.off_items = off;
+  off = align_up(off + sizeof(WorkItem) * plan.items.size(), 256);
+  plan.off_tasks = off;
+  off = align_up(off + sizeof(CombineTask) * plan.tasks.size(), 256);
+  plan.upload_bytes = off;
+  plan.off_slots = off;
+  off = align_up(off + sizeof(float) * slot_floats(head_dim) * size_t(plan.n_slots), 256);
+  plan.bytes = off;
+  return EXTATTN_OK;
+}
+
+}  // namespace extattn

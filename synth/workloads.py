@@ -44,11 +44,16 @@ def round_to_bf16(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     bf16 results, ``bits`` the bf16 bit patterns as uint16. Inputs are finite.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
-    vals = (r.astype(np.uint32) << 16).view(np.float32)
-    return vals, r
+    u = x.view(np.uint32)
+    # finite inputs stay below 0xFF800000, so the sums cannot wrap in uint32
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += u
+    t >>= np.uint32(16)
+    r = t.astype(np.uint16)
+    t <<= np.uint32(16)
+    return t.view(np.float32), r
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

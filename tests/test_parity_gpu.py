@@ -1,0 +1,151 @@
+"""Parity of the HIP library against the CPU oracle (needs a gfx950 GPU).
+
+Every test calls the library through its C ABI (ctypes binding) on seeded
+synthetic inputs and compares element by element with the fp64 oracle:
+bf16 inputs with fp32 accumulation within max abs 2e-2 / mean abs 2e-3
+(lse within 1e-3); fp32 within 1e-5. Chunk plans must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunked_prefill_attention_extend_amd as ext
+from synth import custom_workload, make_workload
+from tests.harness import PagedCache, check_launch, compare, dev_tensor, log, oracle_rows, run_launch, run_planned
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_f32_all_chunks():
+    log("tiny_f32: 64 tokens, C=16, fp32")
+    res = run_planned(make_workload("tiny_f32"))
+    assert len(res) == 4
+
+
+def test_prompt4000_all_chunks_all_rows():
+    log("prompt4000: 8 chunks, every row")
+    res = run_planned(make_workload("prompt4000"))
+    assert len(res) == 8
+
+
+def test_prefix_cache32k_sampled_rows():
+    log("prefix_cache32k: 2 chunks at P=16384/24576, sampled rows")
+    res = run_planned(make_workload("prefix_cache32k"), rows_per_chunk=48)
+    assert len(res) == 2
+
+
+def test_mixed_budget2048():
+    w = make_workload("mixed_budget2048")
+    log("mixed_budget2048: 64 decode rows + 1984-row chunk in one launch")
+    out, lse, q_off, q = run_launch(w)
+    rng = np.random.default_rng(3)
+    chunk_rows = np.unique(np.concatenate([[0, 1, 991, 1982, 1983], rng.choice(1984, 120, replace=False)]))
+    check_launch(w, out, lse, q_off, q, row_sample={64: chunk_rows}, what="mixed step")
+
+
+def test_sweep128k_sampled_chunks():
+    log("sweep128k: 128 chunks appended, chunks 0, 1, 64, 127 compared on sampled rows")
+    res = run_planned(make_workload("sweep128k"), check_chunks=[0, 1, 64, 127], rows_per_chunk=12)
+    assert len(res) == 4
+
+
+@pytest.mark.parametrize("case", [
+    # (launches, Hq, Hkv, D)
+    ([(37, 100)], 28, 4, 128),            # group of 7, ragged tile and ragged key tail
+    ([(0, 1)], 8, 8, 128),                # first token of a prompt: one key
+    ([(0, 333)], 16, 2, 64),              # head_dim 64, empty rectangle
+    ([(1000, 3), (5, 4)], 32, 4, 128),    # short verify rows (split path), 24 and 32 rows
+    ([(77, 5)], 64, 8, 128),              # 40 rows: one partial chunk tile
+    ([(300, 17)], 64, 1, 128),            # one KV head for 64 query heads
+    ([(4095, 1), (16, 1), (1, 1)], 32, 8, 64),  # decode rows, D=64
+])
+def test_edge_cases(case):
+    launches, hq, hkv, d = case
+    w = custom_workload(len(launches) * 100 + hq + d, launches, hq, hkv, d)
+    log(f"edge case {launches} Hq={hq} Hkv={hkv} D={d}")
+    out, lse, q_off, q = run_launch(w)
+    check_launch(w, out, lse, q_off, q, what=f"edge {launches}")
+
+
+def test_fp32_mixed_and_gqa():
+    w = custom_workload(7, [(50, 30), (129, 1), (0, 70)], 8, 2, 128, dtype="f32", mult=1.0)
+    log("fp32 mixed launch with GQA")
+    out, lse, q_off, q = run_launch(w)
+    check_launch(w, out, lse, q_off, q, what="fp32 mixed")
+
+
+def test_request_order_invariance():
+    w = custom_workload(11, [(500, 1), (200, 300), (31, 1), (1000, 129)], 32, 8, 128)
+    o1, l1, off1, _ = run_launch(w)
+    o2, l2, off2, _ = run_launch(w, order=[3, 1, 0, 2])
+    for r in w.requests:
+        e = r.launch[1]
+        a = o1[off1[r.index]:off1[r.index] + e]
+        b = o2[off2[r.index]:off2[r.index] + e]
+        assert torch.equal(a, b), f"request {r.index} depends on its place in the launch"
+
+
+def test_block_permutation_and_determinism():
+    launches = [(700, 200), (65, 1)]
+    w1 = custom_workload(21, launches, 32, 8, 128, permute=True)
+    w2 = custom_workload(21, launches, 32, 8, 128, permute=False)
+    o1, l1, _, _ = run_launch(w1)
+    o1b, l1b, _, _ = run_launch(w1)
+    o2, l2, _, _ = run_launch(w2)
+    assert torch.equal(o1, o1b) and torch.equal(l1, l1b), "repeat run differs"
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "result depends on physical block placement"
+
+
+def test_decode_row_batch_invariance():
+    w = custom_workload(31, [(2000, 1), (900, 600)], 32, 8, 128)
+    out, lse, q_off, q = run_launch(w)
+    alone = custom_workload(31, [(2000, 1)], 32, 8, 128)
+    o2, l2, _, _ = run_launch(alone)
+    assert torch.equal(out[q_off[0]:q_off[0] + 1], o2), "decode row differs when launched with a chunk"
+
+
+def test_kv_append_layout():
+    w = custom_workload(41, [(10, 40)], 8, 4, 128, permute=True)
+    r = w.requests[0]
+    cache = PagedCache(w, fill=0.0)
+    k = w.k(r, 0, 50)
+    v = w.v(r, 0, 50)
+    cache.append([0], [0], k[:10], v[:10], [10])
+    cache.append([0], [10], k[10:], v[10:], [40])
+    kc = cache.k.float().cpu().numpy()
+    vc = cache.v.float().cpu().numpy()
+    for p in range(50):
+        b, s = r.blocks[p // 16], p % 16
+        assert np.array_equal(kc[b, :, s, :], k[p]), f"K of token {p}"
+        assert np.array_equal(vc[b, :, :, s], v[p]), f"V of token {p}"
+
+
+def test_invalid_block_ids_are_counted_not_read():
+    w = custom_workload(51, [(40, 8)], 8, 8, 128)
+    cache = PagedCache(w, fill=0.0)
+    r = w.requests[0]
+    cache.append([0], [0], w.k(r, 0, 48), w.v(r, 0, 48), [48])
+    bad = cache.bt.clone()
+    bad[0, 1] = w.num_blocks + 1000
+    q = dev_tensor(w.q(r, 40, 48), w.dtype)
+    out = torch.empty_like(q)
+    nbytes = ext.workspace_bytes([40], [8], 8, 8, 128, ext.EXTATTN_BF16)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    ext.extend_attention(q, cache.k, cache.v, bad, [40], [8], w.scale, out, None, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) > 0
+    assert torch.isfinite(out.float()).all()
+
+
+def test_device_argument_errors():
+    w = custom_workload(61, [(16, 16)], 8, 2, 128)
+    cache = PagedCache(w, fill=0.0)
+    q = torch.zeros((16, 8, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    with pytest.raises(ValueError):
+        ext.extend_attention(q, cache.k, cache.v, cache.bt, [16], [16], -1.0, out)
+    with pytest.raises(ValueError):
+        ext.extend_attention(q, cache.k, cache.v, cache.bt, [16000], [16], 0.1, out)
+    small = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        ext.extend_attention(q, cache.k, cache.v, cache.bt, [16], [16], 0.1, out, workspace=small)
