@@ -1,0 +1,268 @@
+"""Benchmark of chunked-prefill extend attention on one MI355X.
+
+A step is one pass of the whole hot path over the 128-chunk 128k-token sweep:
+for each of the 128 chunks (P = 1024 t, E = 1024), append the chunk's K/V to the
+paged cache, then run extend attention for its 1024 query rows over keys
+0 .. P+i (64 query heads, 8 KV heads, head dim 128, bf16, block size 16,
+seeded permuted block table). ``value`` is the sweep's algorithmic FLOPs
+(4 * D * Hq * unmasked query-key pairs, 281.48 TFLOP) divided by the measured
+step time, with all inputs resident in HBM before the timed region.
+
+The JSON line also carries:
+* roofline: the attention kernel's achieved TFLOP/s over its own launches
+  (HIP events on the launch stream around every extend_attention call),
+  against the bf16 dense MFMA peak;
+* mixed_step: the 2048-token mixed step (64 decode rows + a 1984-row chunk in
+  one launch); decode-row HBM GB/s measured on the same launch with the chunk
+  request removed, against the 8 TB/s HBM peak;
+* cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4 SIMD x 1024 bf16 FLOP/clk x 2.4 GHz (dense)
+PEAK_HBM_GBS = 8000.0
+
+SWEEP = dict(n=131072, chunk=1024, hq=64, hkv=8, d=128)
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def sweep_flops(chunks, hq, d) -> int:
+    return 4 * d * hq * sum(e * p + e * (e + 1) // 2 for p, e in chunks)
+
+
+def setup_sweep(torch, ext, synth):
+    n, c, hq, hkv, d = SWEEP["n"], SWEEP["chunk"], SWEEP["hq"], SWEEP["hkv"], SWEEP["d"]
+    w = synth.make_workload("sweep128k")
+    plan = ext.chunk_plan(n, c, 0.0)["chunks"]
+    dev = "cuda"
+    bf = torch.bfloat16
+    q = synth.device_normal((n, hq, d), 5001, 0.5, bf)
+    k_new = synth.device_normal((n, hkv, d), 5002, 0.5, bf)
+    v_new = synth.device_normal((n, hkv, d), 5003, 0.5, bf)
+    k_cache = torch.zeros((w.num_blocks, hkv, 16, d), dtype=bf, device=dev)
+    v_cache = torch.zeros((w.num_blocks, hkv, d, 16), dtype=bf, device=dev)
+    bt = torch.from_numpy(w.block_table()).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((n, hq), dtype=torch.float32, device=dev)
+    ws_bytes = max(ext.workspace_bytes([p], [e], hq, hkv, d, ext.EXTATTN_BF16) for p, e in plan)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    kv_ws = torch.empty(4096, dtype=torch.uint8, device=dev)
+    return dict(w=w, plan=plan, q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, bt=bt,
+                out=out, lse=lse, ws=ws, kv_ws=kv_ws, scale=w.scale)
+
+
+def sweep_step(ext, s, events=None):
+    """One pass over the 128 chunks. ``events``: list of (start, end) pairs
+    recorded around each extend_attention call."""
+    for t, (p, e) in enumerate(s["plan"]):
+        ext.kv_append(s["k_new"][p:p + e], s["v_new"][p:p + e], s["k_cache"], s["v_cache"], s["bt"], [p], [e],
+                      workspace=s["kv_ws"])
+        if events is not None:
+            events[t][0].record()
+        ext.extend_attention(s["q"][p:p + e], s["k_cache"], s["v_cache"], s["bt"], [p], [e], s["scale"],
+                             s["out"][p:p + e], s["lse"][p:p + e], workspace=s["ws"])
+        if events is not None:
+            events[t][1].record()
+
+
+def mixed_step_bench(torch, ext, synth, reps: int = 10):
+    """2048-token mixed step: one launch with 64 decode rows and a 1984-row chunk."""
+    w = synth.make_workload("mixed_budget2048")
+    dev = "cuda"
+    bf = torch.bfloat16
+    reqs = w.requests
+    hq, hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
+    k_cache = torch.zeros((w.num_blocks, hkv, 16, d), dtype=bf, device=dev)
+    v_cache = torch.zeros((w.num_blocks, hkv, d, 16), dtype=bf, device=dev)
+    bt_all = w.block_table()
+    # fill each request's context (untimed)
+    for r in reqs:
+        p, e = r.launch
+        kk = synth.device_normal((p + e, hkv, d), 6000 + r.index, 0.5, bf)
+        vv = synth.device_normal((p + e, hkv, d), 7000 + r.index, 0.5, bf)
+        ext.kv_append(kk, vv, k_cache, v_cache, torch.from_numpy(bt_all[r.index:r.index + 1]).to(dev), [0], [p + e])
+    prefix = [r.launch[0] for r in reqs]
+    extend = [r.launch[1] for r in reqs]
+    q = synth.device_normal((sum(extend), hq, d), 6999, 0.5, bf)
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=dev)
+    bt = torch.from_numpy(bt_all).to(dev)
+    ws = torch.empty(ext.workspace_bytes(prefix, extend, hq, hkv, d, ext.EXTATTN_BF16), dtype=torch.uint8,
+                     device=dev)
+    dec = [i for i, r in enumerate(reqs) if r.launch[1] == 1]
+    bt_dec = torch.from_numpy(bt_all[dec]).to(dev)
+    q_dec = q[:len(dec)] if dec == list(range(len(dec))) else None
+    assert q_dec is not None, "decode rows are expected first"
+    out_dec = torch.empty_like(q_dec)
+    lse_dec = torch.empty((len(dec), hq), dtype=torch.float32, device=dev)
+    flush = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        ts = []
+        for i in range(reps + 2):
+            flush.fill_(i & 0xFF)   # evict the 256 MB last-level cache between repetitions
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(a.elapsed_time(b) * 1e-3)
+        return float(np.median(ts))
+
+    t_mix = timed(lambda: ext.extend_attention(q, k_cache, v_cache, bt, prefix, extend, w.scale, out, lse,
+                                               workspace=ws))
+    t_dec = timed(lambda: ext.extend_attention(q_dec, k_cache, v_cache, bt_dec, [prefix[i] for i in dec],
+                                               [1] * len(dec), w.scale, out_dec, lse_dec, workspace=ws))
+    dec_bytes = 0
+    for i in dec:
+        L = prefix[i] + 1
+        dec_bytes += 2 * L * hkv * d * 2 + 2 * hq * d * 2 + 4 * hq + 4 * math.ceil(L / 16)
+    chunk = [(p, e) for p, e in zip(prefix, extend) if e > 1]
+    chunk_flops = sweep_flops(chunk, hq, d)
+    return {
+        "workload": "mixed_budget2048: 64 decode rows (context U{512..8192}) + 1984-row chunk at P=6144, "
+                    "32 q / 8 kv heads, D=128, bf16, one launch",
+        "ms_mixed_launch": t_mix * 1e3,
+        "ms_decode_rows_only": t_dec * 1e3,
+        "decode_bytes": dec_bytes,
+        "decode_GBps": dec_bytes / t_dec / 1e9,
+        "decode_frac_hbm_peak": dec_bytes / t_dec / 1e9 / PEAK_HBM_GBS,
+        "chunk_flops": chunk_flops,
+        "mixed_lower_bound_ms": max(chunk_flops / (PEAK_BF16_TFLOPS * 1e12), dec_bytes / (PEAK_HBM_GBS * 1e9)) * 1e3,
+    }
+
+
+def cpu_baseline(target_s: float = 15.0):
+    """Time the CPU oracle on sampled rows of the sweep (chunk 64, P = 65536)."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = synth.make_workload("sweep128k")
+    req = w.requests[0]
+    p0 = 64 * 1024
+    kk = w.k(req, 0, p0 + 1024)
+    vv = w.v(req, 0, p0 + 1024)
+    rng = np.random.default_rng(0)
+    rows = rng.permutation(1024)
+    flops = 0
+    done = 0
+    t0 = time.perf_counter()
+    for r in rows:
+        pos = p0 + int(r)
+        q = w.q(req, pos, pos + 1)
+        oracle.attend_rows(q, kk, vv, [pos], w.scale)
+        flops += 4 * w.head_dim * w.n_q_heads * (pos + 1)
+        done += 1
+        if time.perf_counter() - t0 > target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} query rows (all 64 heads) of sweep chunk 64 (P=65536), fp64 NumPy, "
+                      f"{dt:.1f} s; affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import chunked_prefill_attention_extend_amd as ext
+    import synth
+
+    ext.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    log("setting up the 128-chunk sweep")
+    s = setup_sweep(torch, ext, synth)
+    flops = sweep_flops(s["plan"], SWEEP["hq"], SWEEP["d"])
+    nchunk = len(s["plan"])
+    for i in range(args.warmup):
+        sweep_step(ext, s)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(nchunk)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        sweep_step(ext, s, [list(p) for p in events[k]])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {dt:.3f} s")
+    kern_s = sum(a.elapsed_time(b) for step in events for a, b in step) * 1e-3 / args.steps
+    per_launch_s = kern_s / nchunk
+    achieved = flops / nchunk / per_launch_s / 1e12
+    ms = dt / args.steps * 1e3
+    value = flops / (dt / args.steps) / 1e12
+
+    mixed = None
+    if not args.no_mixed:
+        log("mixed step")
+        mixed = mixed_step_bench(torch, ext, synth)
+    base = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample)")
+        base = cpu_baseline()
+
+    line = {
+        "metric": "extend-attn bf16 TFLOP/s & % MFMA peak; mixed-step decode HBM GB/s, 1 GPU",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "sweep128k: N=131072 tokens, C=1024 (128 chunks, P=1024t, E=1024), append + "
+                               "extend per chunk, 64 q / 8 kv heads, D=128, bf16, paged block 16, permuted blocks",
+                   "flops_per_step": flops, "chunks": nchunk},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "attn_bf16_kernel<128>",
+                     "avg_launch_ms": per_launch_s * 1e3, "flops_per_launch": flops / nchunk},
+        "mixed_step": mixed,
+        "cpu_baseline": base,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -320,7 +320,7 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it) {
     const int32_t p0 = lb0 < nblk ? bt[lb0] : -1;
     const int32_t p1 = lb0 + 1 < nblk ? bt[lb0 + 1] : -1;
     const bool ok0 = block_ok(p0, a.num_blocks), ok1 = block_ok(p1, a.num_blocks);
-    if (wave == 0 && lane == 0) {
+    if (lane == 0) {
       if (lb0 < nblk && !ok0) atomicAdd(a.err, 1);
       if (lb0 + 1 < nblk && !ok1) atomicAdd(a.err, 1);
     }

@@ -16,6 +16,7 @@ from .workloads import (  # noqa: F401
     block_permutation,
     custom_workload,
     decode_context_lengths,
+    device_normal,
     make_workload,
     round_to_bf16,
     token_values,

@@ -210,3 +210,16 @@ def custom_workload(seed: int, launches: list[tuple[int, int]], n_q_heads: int, 
         scale = float(np.float32(1.0 / math.sqrt(head_dim)))
     return Workload(f"custom{seed}", index, n_q_heads, n_kv_heads, head_dim, dtype, mult, scale, 16,
                     nb, reqs)
+
+
+def device_normal(shape, seed: int, mult: float, dtype, device="cuda"):
+    """Seeded standard-normal values drawn on the device (torch Philox), times
+    ``mult`` in fp32, rounded to ``dtype``. Used where the bench needs gigabytes
+    of inputs quickly; parity tests use the NumPy streams above."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+    if mult != 1.0:
+        x.mul_(mult)
+    return x.to(dtype)
