@@ -15,9 +15,9 @@
 //  * Chunk items: 128 rows, the 4 waves hold 32 rows each; K/V tiles of 64
 //    keys are copied from the paged cache into LDS once per workgroup
 //    (double buffered, one barrier per tile) and read by all 4 waves.
-//  * Split items (<= 32 rows: decode rows, short verify rows): every wave
+//  * Split items (<= 16 rows: decode rows, short verify rows): every wave
 //    reads its own part of the key range straight from HBM into MFMA operand
-//    registers; no LDS.
+//    registers (no LDS) and leaves a partial result for the combine kernel.
 //
 // The contraction runs transposed: S^T = K Q^T and O^T = V^T P^T on
 // v_mfma_f32_32x32x16_bf16. A lane then owns one query row (column l % 32 of
@@ -181,33 +181,49 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
 
+  // Global -> register staging of one K/V tile. Loads are unconditional (an
+  // invalid block id reads block 0 instead) so that nothing waits on them until
+  // the tile is written to LDS one iteration later; the zeroing of invalid
+  // blocks and of keys past the sequence end happens at that point.
   u32x4 kreg[LOADS], vreg[LOADS];
+  int32_t ids[LOADS];
+  uint32_t okbits = 0;
+  auto fetch_ids = [&](int j) {
+#pragma unroll
+    for (int x = 0; x < LOADS; ++x) {
+      const int lb = j * (kKeyTile / kBlockSize) + (tid + kThreads * x) / BLK_PIECES;
+      ids[x] = lb < nblk ? bt[lb] : -1;
+    }
+  };
   auto load_tile = [&](int j) {
+    okbits = 0;
 #pragma unroll
     for (int x = 0; x < LOADS; ++x) {
       const int i = tid + kThreads * x;
-      const int b = i / BLK_PIECES, off = i % BLK_PIECES;
-      const int lb = j * (kKeyTile / kBlockSize) + b;
-      const int32_t phys = lb < nblk ? bt[lb] : -1;
-      const bool ok = block_ok(phys, a.num_blocks);
-      if (lb < nblk && !ok && off == 0) atomicAdd(a.err, 1);
-      const int64_t base = (int64_t(phys) * a.hkv + g) * (kBlockSize * D) + off * 8;
-      kreg[x] = ok ? *reinterpret_cast<const u32x4*>(kc + base) : zero4();
-      const u32x4 vv = ok ? *reinterpret_cast<const u32x4*>(vc + base) : zero4();
-      vreg[x] = clip_keys(vv, lb * kBlockSize + (off & 1) * 8, kv_len);
+      const int off = i % BLK_PIECES;
+      const bool ok = block_ok(ids[x], a.num_blocks);
+      okbits |= uint32_t(ok) << x;
+      const int64_t base = (int64_t(ok ? ids[x] : 0) * a.hkv + g) * (kBlockSize * D) + off * 8;
+      kreg[x] = *reinterpret_cast<const u32x4*>(kc + base);
+      vreg[x] = *reinterpret_cast<const u32x4*>(vc + base);
+      const int lb = j * (kKeyTile / kBlockSize) + i / BLK_PIECES;
+      if (!ok && lb < nblk && off == 0) atomicAdd(a.err, 1);
     }
   };
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](int stage, int j) {
     unsigned char* ks_ = smem + stage * STAGE;
     unsigned char* vs_ = ks_ + KT_BYTES;
 #pragma unroll
     for (int x = 0; x < LOADS; ++x) {
       const int i = tid + kThreads * x;
       const int b = i / BLK_PIECES, off = i % BLK_PIECES;
+      const bool ok = (okbits >> x) & 1u;
       const int kr = b * kBlockSize + off / NC, kp = off % NC;
-      *reinterpret_cast<u32x4*>(ks_ + kr * (D * 2) + ((kp ^ (kr % NC)) << 4)) = kreg[x];
+      *reinterpret_cast<u32x4*>(ks_ + kr * (D * 2) + ((kp ^ (kr % NC)) << 4)) = ok ? kreg[x] : zero4();
+      const int lb = j * (kKeyTile / kBlockSize) + b;
+      const u32x4 vv = ok ? clip_keys(vreg[x], lb * kBlockSize + (off & 1) * 8, kv_len) : zero4();
       const int d = off >> 1, vp = b * 2 + (off & 1);
-      *reinterpret_cast<u32x4*>(vs_ + d * VROW + ((vp ^ ((d >> 1) & 7)) << 4)) = vreg[x];
+      *reinterpret_cast<u32x4*>(vs_ + d * VROW + ((vp ^ ((d >> 1) & 7)) << 4)) = vv;
     }
   };
 
@@ -260,16 +276,24 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   const int t0 = it.key_begin / kKeyTile;
   const int t1 = (it.key_end + kKeyTile - 1) / kKeyTile;
   if (t0 < t1) {
+    fetch_ids(t0);
     load_tile(t0);
-    store_tile(0);
-    if (t0 + 1 < t1) load_tile(t0 + 1);
+    store_tile(0, t0);
+    if (t0 + 1 < t1) {
+      fetch_ids(t0 + 1);
+      load_tile(t0 + 1);
+      if (t0 + 2 < t1) fetch_ids(t0 + 2);
+    }
     __syncthreads();
     for (int j = t0; j < t1; ++j) {
       const int stage = (j - t0) & 1;
       compute(stage, j);
       if (j + 1 < t1) {
-        store_tile(stage ^ 1);
-        if (j + 2 < t1) load_tile(j + 2);
+        store_tile(stage ^ 1, j + 1);
+        if (j + 2 < t1) {
+          load_tile(j + 2);
+          if (j + 3 < t1) fetch_ids(j + 3);
+        }
       }
       __syncthreads();
     }
@@ -278,43 +302,64 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
 }
 
 // ---------------------------------------------------------------------------
-// Split items: <= 32 rows, each wave streams its own keys from HBM.
+// Split items: <= 16 rows (decode rows, short verify rows); each wave streams
+// its own part of the key range from HBM straight into MFMA operand registers,
+// two 32-key tiles in flight. These run on v_mfma_f32_16x16x32_bf16 (16 query
+// rows per wave). Accumulator element i of lane l belongs to query row l % 16
+// and MFMA row 4 (l / 16) + i; MFMA row r of key block b holds key
+// 8 (r / 4) + 4 b + r % 4 of the tile, so each lane's P^T operand (4 values
+// from block 0, 4 from block 1) covers 8 consecutive keys.
 // ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
 template <int D>
 __device__ void split_item(const AttnArgs& a, const WorkItem& it) {
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
+  constexpr int KS = D / 32;  // 32-wide k-steps over the head dim
+  constexpr int DB = D / 16;  // 16-feature blocks of O^T
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
   const SeqInfo si = a.seqs[it.seq];
   const int G = a.group, g = it.kv_head;
   const int kv_len = si.prefix + si.extend;
-  const bool valid = l32 < it.nrows;
-  const int pos = valid ? l32 / G : 0;
-  const int hh = valid ? l32 - pos * G : 0;
+  const bool valid = l16 < it.nrows;
+  const int pos = valid ? l16 / G : 0;
+  const int hh = valid ? l16 - pos * G : 0;
   const int64_t orow = int64_t(si.q_off + pos) * a.hq + g * G + hh;
   const int lim = valid ? min(si.prefix + pos, it.key_end - 1) : -1;
 
   u32x4 qf[KS];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + orow * D + hi * 8;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + orow * D + q4 * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = valid ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : zero4();
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = valid ? *reinterpret_cast<const u32x4*>(qp + ks * 32) : zero4();
   }
   const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
   const int nblk = (kv_len + kBlockSize - 1) / kBlockSize;
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
 
-  f32x16 o[DB];
+  f32x4 o[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  const int nt = (it.key_end - it.key_begin + kSplitTile - 1) / kSplitTile;
-  const int tw0 = wave * nt / 4, tw1 = (wave + 1) * nt / 4;
-  const int krow = key_of_row(l32);
-  for (int jj = tw0; jj < tw1; ++jj) {
+  // Keys (within the 32-key tile) this lane loads as MFMA rows of blocks 0 / 1.
+  const int kbase = 8 * (l16 >> 2) + (l16 & 3);
+  struct Tile {
+    u32x4 kf[2][KS];
+    u32x4 vf[DB];
+    int kt;
+    bool ok0, ok1;
+  };
+  // Loads are unconditional (invalid block ids read block 0); validity and the
+  // sequence end are applied when the tile is consumed, so the next tile's
+  // loads stay in flight while this one is computed.
+  auto load = [&](int jj, Tile& T) {
     const int kt = it.key_begin + jj * kSplitTile;
     const int lb0 = kt / kBlockSize;
     const int32_t p0 = lb0 < nblk ? bt[lb0] : -1;
@@ -324,42 +369,97 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it) {
       if (lb0 < nblk && !ok0) atomicAdd(a.err, 1);
       if (lb0 + 1 < nblk && !ok1) atomicAdd(a.err, 1);
     }
-    // K operand: this lane's MFMA row holds key kt + krow.
-    const int key = kt + krow;
-    const int32_t pk = krow < kBlockSize ? p0 : p1;
-    const bool okk = (krow < kBlockSize ? ok0 : ok1) && key < kv_len;
-    const uint16_t* kp = kc + ((int64_t(pk) * a.hkv + g) * kBlockSize + (key % kBlockSize)) * D + hi * 8;
-    u32x4 kf[KS];
+    const int32_t s0 = ok0 ? p0 : 0, s1 = ok1 ? p1 : 0;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = okk ? *reinterpret_cast<const u32x4*>(kp + ks * 16) : zero4();
-    // V^T operand: feature db*32 + l32, keys kt + 16 v + 8 hi .. +8.
-    u32x4 vf[DB][2];
+    for (int b = 0; b < 2; ++b) {
+      const int koff = kbase + 4 * b;  // < 32; block koff / 16
+      const int32_t pk = koff < kBlockSize ? s0 : s1;
+      const uint16_t* kp = kc + ((int64_t(pk) * a.hkv + g) * kBlockSize + (koff % kBlockSize)) * D + q4 * 8;
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const int32_t pv = v ? p1 : p0;
-      const bool okv = v ? ok1 : ok0;
-      const uint16_t* vp = vc + (int64_t(pv) * a.hkv + g) * (kBlockSize * D) + hi * 8;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x4 raw = okv ? *reinterpret_cast<const u32x4*>(vp + (db * 32 + l32) * kBlockSize) : zero4();
-        vf[db][v] = clip_keys(raw, kt + 16 * v + 8 * hi, kv_len);
-      }
+      for (int ks = 0; ks < KS; ++ks) T.kf[b][ks] = *reinterpret_cast<const u32x4*>(kp + ks * 32);
     }
-    f32x16 s[1];
-    s[0] = f32x16{};
+    const int32_t pv = q4 < 2 ? s0 : s1;
+    const uint16_t* vp = vc + (int64_t(pv) * a.hkv + g) * (kBlockSize * D) + 8 * (q4 & 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s[0] = mfma32(kf[ks], qf[ks], s[0]);
+    for (int db = 0; db < DB; ++db) T.vf[db] = *reinterpret_cast<const u32x4*>(vp + (db * 16 + l16) * kBlockSize);
+    T.kt = kt;
+    T.ok0 = ok0;
+    T.ok1 = ok1;
+  };
+  auto compute = [&](Tile& T) {
+    const int kt = T.kt;
+    f32x4 sc[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (kt + key_of_elem(i, hi) > lim) s[0][i] = -INFINITY;
-    u32x4 pf[1][2];
-    softmax_step<1, DB>(s, o, m, l, a.scale_log2, pf);
+    for (int b = 0; b < 2; ++b) {
+      const int koff = kbase + 4 * b;
+      const bool okk = (koff < kBlockSize ? T.ok0 : T.ok1) && kt + koff < kv_len;
+      sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int ks = 0; ks < KS; ++ks) sc[b] = mfma16(okk ? T.kf[b][ks] : zero4(), qf[ks], sc[b]);
 #pragma unroll
-      for (int v = 0; v < 2; ++v) o[db] = mfma32(vf[db][v], pf[0][v], o[db]);
+      for (int i = 0; i < 4; ++i)
+        if (kt + 8 * q4 + 4 * b + i > lim) sc[b][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[b][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx * a.scale_log2);
+    if (mnew > m) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      l *= alpha;
+      m = mnew;
+    }
+    const float msafe = (m == -INFINITY) ? 0.f : m;
+    u32x4 pf;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[b][0], a.scale_log2, -msafe));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][1], a.scale_log2, -msafe));
+      const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[b][2], a.scale_log2, -msafe));
+      const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[b][3], a.scale_log2, -msafe));
+      l += (p0 + p1) + (p2 + p3);
+      pf[2 * b] = pack2(p0, p1);
+      pf[2 * b + 1] = pack2(p2, p3);
+    }
+    const bool okv = q4 < 2 ? T.ok0 : T.ok1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const u32x4 vv = okv ? clip_keys(T.vf[db], kt + 8 * q4, kv_len) : zero4();
+      o[db] = mfma16(vv, pf, o[db]);
+    }
+  };
+
+  const int nt = (it.key_end - it.key_begin + kSplitTile - 1) / kSplitTile;
+  const int tw0 = wave * nt / 4, tw1 = (wave + 1) * nt / 4;
+  Tile ta, tb;
+  if (tw0 < tw1) load(tw0, ta);
+  for (int jj = tw0; jj < tw1; jj += 2) {
+    if (jj + 1 < tw1) load(jj + 1, tb);
+    compute(ta);
+    if (jj + 1 < tw1) {
+      if (jj + 2 < tw1) load(jj + 2, ta);
+      compute(tb);
+    }
   }
-  write_row<D>(a, o, m, l, valid, hi, orow, it.slot + wave, l32);
+
+  // Partial result of this wave: normalised o (fp32) and natural-log lse.
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
+  if (!valid) return;
+  float* sl = a.slots + size_t(it.slot + wave) * slot_floats(D);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    float4 v = {o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
+    *reinterpret_cast<float4*>(sl + l16 * D + db * 16 + 4 * q4) = v;
+  }
+  if (q4 == 0) sl[kRowsPerWave * D + l16] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
 }
 
 template <int D>

@@ -16,6 +16,7 @@ constexpr int kRowsPerTile = 128; // chunk path: 4 waves x 32 rows share each K/
 constexpr int kKeyTile = 64;      // chunk path: keys per LDS K/V tile
 constexpr int kSplitTile = 32;    // split path: keys per register K/V tile
 constexpr int kSplitKeys = 1024;  // split path: keys per workgroup (4 waves)
+constexpr int kSplitRows = 16;    // split path: at most this many rows (one 16-row MFMA block)
 
 // Per-request metadata copied to the workspace.
 struct SeqInfo {
@@ -27,7 +28,7 @@ struct SeqInfo {
 
 enum : int32_t {
   kItemChunk = 0,  // 128 rows of one (request, KV head); 4 waves share LDS K/V tiles
-  kItemSplit = 1,  // <= 32 rows; each of the 4 waves takes its own part of the key range
+  kItemSplit = 1,  // <= 16 rows; each of the 4 waves takes its own part of the key range
 };
 
 // One workgroup's work. Rows are flattened per (request, KV head) as

@@ -40,8 +40,8 @@ int chunk_plan_impl(int64_t n_tokens, int64_t chunk_size, double hit_rate, int64
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Work list of one launch. Requests whose E * group rows fit one wave (decode
-// rows, short verify rows) take the split path: the key range is cut into
+// Work list of one launch. Requests whose E * group rows fit one 16-row MFMA
+// block (decode rows, short verify rows) take the split path: the key range is cut into
 // kSplitKeys pieces, each piece into four per-wave parts, and the partial
 // results are merged by the combine kernel. Longer chunks take the chunk path:
 // 128-row tiles over their whole causal key range.
@@ -64,7 +64,7 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
     for (int32_t r = 0; r < num_seqs; ++r) {
       const int64_t rows = int64_t(extend[r]) * group;
       const int64_t kv_len = int64_t(prefix[r]) + extend[r];
-      if (rows <= kRowsPerWave) {
+      if (rows <= kSplitRows) {
         const int64_t nwg = (kv_len + kSplitKeys - 1) / kSplitKeys;
         for (int32_t g = 0; g < hkv; ++g) {
           const int64_t slot0 = plan.n_slots;

@@ -54,7 +54,9 @@ def test_sweep128k_sampled_chunks():
     ([(37, 100)], 28, 4, 128),            # group of 7, ragged tile and ragged key tail
     ([(0, 1)], 8, 8, 128),                # first token of a prompt: one key
     ([(0, 333)], 16, 2, 64),              # head_dim 64, empty rectangle
-    ([(1000, 3), (5, 4)], 32, 4, 128),    # short verify rows (split path), 24 and 32 rows
+    ([(1000, 3), (5, 4)], 32, 4, 128),    # verify rows of 24 and 32 rows (chunk path, one partial tile)
+    ([(500, 2), (64, 3), (2047, 4)], 32, 8, 128),  # verify rows of 8, 12, 16 rows (split path)
+    ([(777, 2)], 64, 8, 64),              # 16 split rows at two positions, D=64
     ([(77, 5)], 64, 8, 128),              # 40 rows: one partial chunk tile
     ([(300, 17)], 64, 1, 128),            # one KV head for 64 query heads
     ([(4095, 1), (16, 1), (1, 1)], 32, 8, 64),  # decode rows, D=64
