@@ -27,6 +27,8 @@
 // a 32-key block is permuted (bits 2 and 3 of the row index swapped) so that
 // each lane's 8 P^T values cover 8 consecutive keys, which makes the V^T
 // operand one 16-byte read of the slot-minor V cache layout.
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace extattn {
@@ -142,21 +144,51 @@ __device__ inline void write_row(const AttnArgs& a, const f32x16 (&o)[D / 32], f
 
 // ---------------------------------------------------------------------------
 // Chunk items: 128 rows, LDS-shared K/V tiles of 64 keys.
+//
+// K/V tiles go from the paged cache straight into LDS (global_load_lds_dwordx4:
+// each lane's 16 bytes land at the instruction's LDS base + 16 * lane), so no
+// registers hold the next tile. Each wave issues 1/4 of a tile per buffer.
+// LDS layouts (per stage):
+//   K: 64 rows (keys) x D bf16; 16-byte piece p of row r sits at position
+//      p ^ swz_k(r), swz_k(r) = key_of_row(r % 16) (mod pieces per row).
+//   V: four sub-tiles, one per 16-key block, each D rows (features) x 16 keys;
+//      half h (8 keys) of row d sits at position h ^ swz_v(d),
+//      swz_v(d) = ((d >> 2) ^ (d >> 3)) & 1.
+// Wave w loads block w of the tile for both K and V, so every direct load has
+// one block (a uniform base address) and a 32-bit per-lane offset.
+// Both keep every aligned group of 8 (and of 16) lanes of a 16-byte LDS read on
+// distinct banks. Tiles that reach past the sequence end or hold an invalid
+// block id are masked when read; all others are read as they are.
 // ---------------------------------------------------------------------------
+__device__ inline int swz_v(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
+
+// Reductions over the two lanes (l, l ^ 32) that hold one query row.
+__device__ inline float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Lazy rescale threshold (log2 units): the running max m is raised only when a
+// tile's max exceeds it by more than this, so softmax weights stay <= 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D>
 __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char* smem) {
+  constexpr int KT = kChunkKeys;                  // keys per tile (one 32x32 S^T block)
   constexpr int NC = D / 8;                       // 16-byte pieces per K row
   constexpr int KS = D / 16;                      // MFMA k-steps over the head dim
   constexpr int DB = D / 32;                      // 32-feature blocks of O^T
-  constexpr int KT_BYTES = kKeyTile * D * 2;      // one K tile (= one V tile)
-  constexpr int STAGE = 2 * KT_BYTES;
-  constexpr int BLK_PIECES = kBlockSize * NC;     // 16-byte pieces per (block, head)
-  constexpr int LOADS = kKeyTile * NC / kThreads; // pieces per thread per tile
-  constexpr int VROW = kKeyTile * 2;              // bytes per V^T row in LDS
-  static_assert(LOADS >= 1, "tile too small for the workgroup");
+  constexpr int KT_BYTES = KT * D * 2;            // one K tile (= one V tile)
+  constexpr int VSUB = D * kBlockSize * 2;        // one V^T sub-tile (16 keys)
+  constexpr int NINST = KT_BYTES / 1024 / 4;      // 1 KB direct loads per wave per tile (K and V each)
+  constexpr int RING = 4;                         // LDS ring slots per operand
+  constexpr int KBUF = 0, VBUF = RING * KT_BYTES; // LDS: K ring, then V ring, then block ids
+  constexpr int IDBUF = 2 * RING * KT_BYTES;
+  static_assert(NINST >= 1, "tile too small for the workgroup");
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  // wave index as a uniform (scalar) value: block bases and LDS destinations stay in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const SeqInfo si = a.seqs[it.seq];
   const int G = a.group, g = it.kv_head;
   const int kv_len = si.prefix + si.extend;
@@ -168,6 +200,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   const int64_t orow = int64_t(si.q_off + pos) * a.hq + g * G + hh;
   const int lim = valid ? min(si.prefix + pos, it.key_end - 1) : -1;
   const int lim_min = min(si.prefix + it.row0 / G, it.key_end - 1);
+  const float c2 = a.scale_log2;
 
   u32x4 qf[KS];
   {
@@ -181,49 +214,66 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
 
-  // Global -> register staging of one K/V tile. Loads are unconditional (an
-  // invalid block id reads block 0 instead) so that nothing waits on them until
-  // the tile is written to LDS one iteration later; the zeroing of invalid
-  // blocks and of keys past the sequence end happens at that point.
-  u32x4 kreg[LOADS], vreg[LOADS];
-  int32_t ids[LOADS];
-  uint32_t okbits = 0;
-  auto fetch_ids = [&](int j) {
+  // K read of k-step ks: row key_of_row(l32), position (2 ks + hi) ^ swz_k(row) =
+  // (2 ks) ^ (hi ^ (l32 & 15)); the row base is a multiple of the row size, so
+  // the offset is k_off0 ^ (ks << 5).
+  const int k_off0 = key_of_row(l32) * (D * 2) + (((hi ^ (l32 & 15)) & (NC - 1)) << 4);
+  const int v_off = l32 * (kBlockSize * 2) + ((hi ^ swz_v(l32)) << 4);
+
+  // Block ids go through a small LDS ring (64 tiles = 128 ids) filled by direct
+  // loads, 32 tiles at a time, so the loop holds no register-destination loads.
+  int32_t* id_ring = reinterpret_cast<int32_t*>(smem + IDBUF);
+  // Copy the ids of tiles [jt, jt + 32) into ring half (jt - t0) / 32 % 2 (wave 0 only).
+  auto fill_ids = [&](int jt, int t0_) {
+    if (wave != 0) return;
+    const int lb = jt * (KT / kBlockSize) + lane;  // 64 ids
+    const int src = lb < nblk ? lb : nblk - 1;     // stay inside the table row
+    const int half = ((jt - t0_) / 32) & 1;
+    __builtin_amdgcn_global_load_lds(bt + src, (lds_ptr_t)(id_ring + half * 64), 4, 0, 0);
+  };
+  struct Ids {
+    int32_t p0, p1;  // uniform block ids (invalid ones replaced by 0)
+    uint32_t ok;     // valid-block mask
+  };
+  auto read_ids = [&](int j, int t0_) -> Ids {
+    const int e = ((j - t0_) & 63) * 2;
+    int32_t v0 = __builtin_amdgcn_readfirstlane(id_ring[e]);
+    int32_t v1 = __builtin_amdgcn_readfirstlane(id_ring[e + 1]);
+    if (j * 2 >= nblk) v0 = -1;
+    if (j * 2 + 1 >= nblk) v1 = -1;
+    const bool ok0 = block_ok(v0, a.num_blocks), ok1 = block_ok(v1, a.num_blocks);
+    if (tid == 0) {
+      if (!ok0 && j * 2 < nblk) atomicAdd(a.err, 1);
+      if (!ok1 && j * 2 + 1 < nblk) atomicAdd(a.err, 1);
+    }
+    return Ids{ok0 ? v0 : 0, ok1 ? v1 : 0, uint32_t(ok0) | (uint32_t(ok1) << 1)};
+  };
+  // Direct loads of one tile: waves 0, 1 load block 0 of the tile, waves 2, 3 block 1;
+  // each wave copies half of its block's K (rows) and half of its V (feature rows).
+  auto issue_k = [&](const Ids& ids, int slot) {
+    unsigned char* dst = smem + KBUF + slot * KT_BYTES;
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(
+        kc + (int64_t(wave < 2 ? ids.p0 : ids.p1) * a.hkv + g) * (kBlockSize * D));
 #pragma unroll
-    for (int x = 0; x < LOADS; ++x) {
-      const int lb = j * (kKeyTile / kBlockSize) + (tid + kThreads * x) / BLK_PIECES;
-      ids[x] = lb < nblk ? bt[lb] : -1;
+    for (int x = 0; x < NINST; ++x) {
+      const int i = wave * NINST + x;  // 1 KB piece of the tile
+      const int n = i * 64 + lane;     // 16-byte slot: row r (key), position c
+      const int r = n / NC, c = n % NC;
+      const uint32_t off = uint32_t(((r & 15) * D + ((c ^ (key_of_row(r & 15) & (NC - 1))) * 8)) * 2);
+      __builtin_amdgcn_global_load_lds(base + off, (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
     }
   };
-  auto load_tile = [&](int j) {
-    okbits = 0;
+  auto issue_v = [&](const Ids& ids, int slot) {
+    unsigned char* dst = smem + VBUF + slot * KT_BYTES;
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(
+        vc + (int64_t(wave < 2 ? ids.p0 : ids.p1) * a.hkv + g) * (kBlockSize * D));
 #pragma unroll
-    for (int x = 0; x < LOADS; ++x) {
-      const int i = tid + kThreads * x;
-      const int off = i % BLK_PIECES;
-      const bool ok = block_ok(ids[x], a.num_blocks);
-      okbits |= uint32_t(ok) << x;
-      const int64_t base = (int64_t(ok ? ids[x] : 0) * a.hkv + g) * (kBlockSize * D) + off * 8;
-      kreg[x] = *reinterpret_cast<const u32x4*>(kc + base);
-      vreg[x] = *reinterpret_cast<const u32x4*>(vc + base);
-      const int lb = j * (kKeyTile / kBlockSize) + i / BLK_PIECES;
-      if (!ok && lb < nblk && off == 0) atomicAdd(a.err, 1);
-    }
-  };
-  auto store_tile = [&](int stage, int j) {
-    unsigned char* ks_ = smem + stage * STAGE;
-    unsigned char* vs_ = ks_ + KT_BYTES;
-#pragma unroll
-    for (int x = 0; x < LOADS; ++x) {
-      const int i = tid + kThreads * x;
-      const int b = i / BLK_PIECES, off = i % BLK_PIECES;
-      const bool ok = (okbits >> x) & 1u;
-      const int kr = b * kBlockSize + off / NC, kp = off % NC;
-      *reinterpret_cast<u32x4*>(ks_ + kr * (D * 2) + ((kp ^ (kr % NC)) << 4)) = ok ? kreg[x] : zero4();
-      const int lb = j * (kKeyTile / kBlockSize) + b;
-      const u32x4 vv = ok ? clip_keys(vreg[x], lb * kBlockSize + (off & 1) * 8, kv_len) : zero4();
-      const int d = off >> 1, vp = b * 2 + (off & 1);
-      *reinterpret_cast<u32x4*>(vs_ + d * VROW + ((vp ^ ((d >> 1) & 7)) << 4)) = vv;
+    for (int x = 0; x < NINST; ++x) {
+      const int i = wave * NINST + x;                          // 1 KB piece of the tile
+      const int d = ((i * 64 + lane) % (VSUB / 16)) / 2;       // feature row within the sub-tile
+      const int cv = lane & 1;                                 // position; holds half cv ^ swz_v(d)
+      const uint32_t off = uint32_t((d * kBlockSize + ((cv ^ swz_v(d)) * 8)) * 2);
+      __builtin_amdgcn_global_load_lds(base + off, (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
     }
   };
 
@@ -232,71 +282,128 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  auto compute = [&](int stage, int j) {
-    const unsigned char* ks_ = smem + stage * STAGE;
-    const unsigned char* vs_ = ks_ + KT_BYTES;
-    f32x16 s[2];
+  // S^T of one tile from K ring slot `slot` (compile-time); K of invalid blocks reads as zero.
+  auto qk = [&](auto slot_tag, uint32_t okm, f32x16& s) {
+    constexpr int slot = decltype(slot_tag)::value;
+    const unsigned char* base = smem + KBUF + slot * KT_BYTES;
+    s = f32x16{};
+    const bool z = !((okm >> (key_of_row(l32) >> 4)) & 1u);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const int kr = kb * 32 + key_of_row(l32);
-      const unsigned char* krow = ks_ + kr * (D * 2);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + (((ks * 2 + hi) ^ (kr % NC)) << 4));
-        s[kb] = mfma32(kf, qf[ks], s[kb]);
-      }
-    }
-    const int kt = j * kKeyTile;
-    if (kt + kKeyTile - 1 > lim_min) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kt + kb * 32 + key_of_elem(i, hi) > lim) s[kb][i] = -INFINITY;
-    }
-    u32x4 pf[2][2];
-    softmax_step<2, DB>(s, o, m, l, a.scale_log2, pf);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = db * 32 + l32;
-      const unsigned char* vrow = vs_ + d * VROW;
-      const int sw = (d >> 1) & 7;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          const int vp = kb * 4 + v * 2 + hi;
-          const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + ((vp ^ sw) << 4));
-          o[db] = mfma32(vf, pf[kb][v], o[db]);
-        }
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 kf = *reinterpret_cast<const u32x4*>(base + (k_off0 ^ (ks << 5)));
+      if (okm != 0x3u && z) kf = zero4();
+      s = mfma32(kf, qf[ks], s);
     }
   };
-
-  const int t0 = it.key_begin / kKeyTile;
-  const int t1 = (it.key_end + kKeyTile - 1) / kKeyTile;
-  if (t0 < t1) {
-    fetch_ids(t0);
-    load_tile(t0);
-    store_tile(0, t0);
-    if (t0 + 1 < t1) {
-      fetch_ids(t0 + 1);
-      load_tile(t0 + 1);
-      if (t0 + 2 < t1) fetch_ids(t0 + 2);
+  // Online softmax of one tile: mask, lazy max update, weights as packed bf16.
+  auto softmax = [&](int j, f32x16& s, u32x4 (&pf)[2]) {
+    const int kt = j * KT;
+    if (kt + KT - 1 > lim_min) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (kt + key_of_elem(i, hi) > lim) s[i] = -INFINITY;
     }
-    __syncthreads();
-    for (int j = t0; j < t1; ++j) {
-      const int stage = (j - t0) & 1;
-      compute(stage, j);
-      if (j + 1 < t1) {
-        store_tile(stage ^ 1, j + 1);
-        if (j + 2 < t1) {
-          load_tile(j + 2);
-          if (j + 3 < t1) fetch_ids(j + 3);
-        }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = pair_max(mx) * c2;
+    // wave-uniform decision; every lane then moves m to its exact new max
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      l *= alpha;
+      m = mnew;
+    }
+    const float msafe = (m == -INFINITY) ? 0.f : m;
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * v + 2 * w], c2, -msafe));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * v + 2 * w + 1], c2, -msafe));
+        pf[v][w] = pack2(p0, p1);
+        ls0 += p0;
+        ls1 += p1;
       }
-      __syncthreads();
+    l += ls0 + ls1;
+  };
+  // O^T += V^T P^T for one tile from V ring slot `slot` (compile-time).
+  auto pv = [&](auto slot_tag, int j, uint32_t okm, const u32x4 (&pf)[2]) {
+    constexpr int slot = decltype(slot_tag)::value;
+    const unsigned char* base = smem + VBUF + slot * KT_BYTES;
+    const int kt = j * KT;
+    const bool clipped = okm != 0x3u || kt + KT > kv_len;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {  // 16-key block of the tile; this lane's keys 16 b + 8 hi .. +8
+        u32x4 vf = *reinterpret_cast<const u32x4*>(base + v_off + b * VSUB + db * 32 * (kBlockSize * 2));
+        if (clipped) vf = ((okm >> b) & 1u) ? clip_keys(vf, kt + 16 * b + 8 * hi, kv_len) : zero4();
+        o[db] = mfma32(vf, pf[b], o[db]);
+      }
+  };
+
+  const int t0 = it.key_begin / KT;
+  const int t1 = (it.key_end + KT - 1) / KT;
+  const int n = t1 - t0;
+  if (n > 0) {
+    // Pipeline over tiles j = t0 + u: tile j's K sits in K slot u % 4 and its V in
+    // V slot u % 4. Step u computes S(j+1) = QK(j+1) next to the softmax of tile j,
+    // then P(j) V(j); it first issues K(j+3) and V(j+2) (their slots were last read
+    // two steps earlier). Every step issues the same number of vector memory
+    // instructions (ids and tiles past the end load harmless entries), so waiting
+    // for "at most one step's worth outstanding" completes everything older.
+    constexpr int kIssuePerStep = 2 * NINST;  // tile loads per step (the id refills come on top)
+    // Prologue: ids of tiles t0 .. t0+63, then K and V of t0 and t0+1, K of t0+2.
+    fill_ids(t0, t0);
+    fill_ids(t0 + 32, t0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const Ids ids0 = read_ids(t0, t0);
+    issue_k(ids0, 0);
+    issue_v(ids0, 0);
+    const Ids ids1 = read_ids(t0 + 1, t0);
+    issue_k(ids1, 1);
+    issue_v(ids1, 1);
+    Ids pending = read_ids(t0 + 2, t0);  // tile j+2: K issued, V not yet
+    issue_k(pending, 2);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    f32x16 sa, sb;
+    u32x4 pf[2];
+    qk(std::integral_constant<int, 0>{}, ids0.ok, sa);
+    uint32_t ok_j = ids0.ok, ok_j1 = ids1.ok;  // valid-block masks of tiles j, j+1
+    auto step = [&](auto slot_tag, int u, f32x16& scur, f32x16& snext) {
+      constexpr int sl = decltype(slot_tag)::value;  // u % 4
+      const int j = t0 + u;
+      // ids of tiles j+32 .. j+63 replace those of tiles j-32 .. j-1 (long consumed);
+      // first read (tile j+32, by step u+29) comes after two barriers
+      if ((u & 31) == 0 && u > 0) fill_ids(j + 32, t0);
+      const Ids ik = read_ids(j + 3, t0);
+      issue_k(ik, (sl + 3) & 3);
+      issue_v(pending, (sl + 2) & 3);
+      const uint32_t ok_j2 = pending.ok;
+      pending = ik;
+      if (u + 1 < n) qk(std::integral_constant<int, (sl + 1) & 3>{}, ok_j1, snext);
+      softmax(j, scur, pf);
+      pv(std::integral_constant<int, sl>{}, j, ok_j, pf);
+      ok_j = ok_j1;
+      ok_j1 = ok_j2;
+      // Loads issued before this step are complete (in-order completion); a bare
+      // barrier publishes them without waiting for this step's loads.
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(kIssuePerStep) : "memory");
+    };
+    for (int u = 0; u < n; u += 4) {
+      step(std::integral_constant<int, 0>{}, u, sa, sb);
+      if (u + 1 >= n) break;
+      step(std::integral_constant<int, 1>{}, u + 1, sb, sa);
+      if (u + 2 >= n) break;
+      step(std::integral_constant<int, 2>{}, u + 2, sa, sb);
+      if (u + 3 >= n) break;
+      step(std::integral_constant<int, 3>{}, u + 3, sb, sa);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads issued past the end
   }
   write_row<D>(a, o, m, l, valid, hi, orow, it.slot < 0 ? -1 : it.slot + wave, rloc);
 }
@@ -465,7 +572,7 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it) {
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * kKeyTile * D * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 4 * kChunkKeys * D * 2 + 512];
   const WorkItem it = a.items[blockIdx.x];
   if (it.kind == kItemChunk)
     chunk_item<D>(a, it, smem);
