@@ -251,6 +251,7 @@ int extattn_extend_attention(const void* q, const void* k_cache, const void* v_c
   a.tasks = reinterpret_cast<const CombineTask*>(ws + plan.off_tasks);
   a.slots = reinterpret_cast<float*>(ws + plan.off_slots);
   a.err = reinterpret_cast<int32_t*>(ws);
+  a.zero_page = ws + plan.off_zero;
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks;
   a.num_seqs = num_seqs;

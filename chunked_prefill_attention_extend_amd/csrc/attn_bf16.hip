@@ -232,7 +232,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     __builtin_amdgcn_global_load_lds(bt + src, (lds_ptr_t)(id_ring + half * 64), 4, 0, 0);
   };
   struct Ids {
-    int32_t p0, p1;  // uniform block ids (invalid ones replaced by 0)
+    int32_t p0, p1;  // uniform block ids (invalid ones replaced by -1: read the zero page)
     uint32_t ok;     // valid-block mask
   };
   auto read_ids = [&](int j, int t0_) -> Ids {
@@ -246,14 +246,19 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       if (!ok0 && j * 2 < nblk) atomicAdd(a.err, 1);
       if (!ok1 && j * 2 + 1 < nblk) atomicAdd(a.err, 1);
     }
-    return Ids{ok0 ? v0 : 0, ok1 ? v1 : 0, uint32_t(ok0) | (uint32_t(ok1) << 1)};
+    return Ids{ok0 ? v0 : -1, ok1 ? v1 : -1, uint32_t(ok0) | (uint32_t(ok1) << 1)};
   };
   // Direct loads of one tile: waves 0, 1 load block 0 of the tile, waves 2, 3 block 1;
   // each wave copies half of its block's K (rows) and half of its V (feature rows).
+  // Source of this wave's block: the cache, or the zero page for an invalid id.
+  auto block_base = [&](const uint16_t* cache, const Ids& ids) -> const unsigned char* {
+    const int32_t blk = wave < 2 ? ids.p0 : ids.p1;
+    return blk < 0 ? static_cast<const unsigned char*>(a.zero_page)
+                   : reinterpret_cast<const unsigned char*>(cache + (int64_t(blk) * a.hkv + g) * (kBlockSize * D));
+  };
   auto issue_k = [&](const Ids& ids, int slot) {
     unsigned char* dst = smem + KBUF + slot * KT_BYTES;
-    const unsigned char* base = reinterpret_cast<const unsigned char*>(
-        kc + (int64_t(wave < 2 ? ids.p0 : ids.p1) * a.hkv + g) * (kBlockSize * D));
+    const unsigned char* base = block_base(kc, ids);
 #pragma unroll
     for (int x = 0; x < NINST; ++x) {
       const int i = wave * NINST + x;  // 1 KB piece of the tile
@@ -265,8 +270,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   };
   auto issue_v = [&](const Ids& ids, int slot) {
     unsigned char* dst = smem + VBUF + slot * KT_BYTES;
-    const unsigned char* base = reinterpret_cast<const unsigned char*>(
-        vc + (int64_t(wave < 2 ? ids.p0 : ids.p1) * a.hkv + g) * (kBlockSize * D));
+    const unsigned char* base = block_base(vc, ids);
 #pragma unroll
     for (int x = 0; x < NINST; ++x) {
       const int i = wave * NINST + x;                          // 1 KB piece of the tile
@@ -282,16 +286,15 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  // S^T of one tile from K ring slot `slot` (compile-time); K of invalid blocks reads as zero.
-  auto qk = [&](auto slot_tag, uint32_t okm, f32x16& s) {
+  // S^T of one tile from K ring slot `slot` (compile-time). Invalid blocks were
+  // loaded from the zero page; keys past the sequence end are masked later.
+  auto qk = [&](auto slot_tag, f32x16& s) {
     constexpr int slot = decltype(slot_tag)::value;
     const unsigned char* base = smem + KBUF + slot * KT_BYTES;
     s = f32x16{};
-    const bool z = !((okm >> (key_of_row(l32) >> 4)) & 1u);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 kf = *reinterpret_cast<const u32x4*>(base + (k_off0 ^ (ks << 5)));
-      if (okm != 0x3u && z) kf = zero4();
+      const u32x4 kf = *reinterpret_cast<const u32x4*>(base + (k_off0 ^ (ks << 5)));
       s = mfma32(kf, qf[ks], s);
     }
   };
@@ -330,18 +333,20 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       }
     l += ls0 + ls1;
   };
-  // O^T += V^T P^T for one tile from V ring slot `slot` (compile-time).
-  auto pv = [&](auto slot_tag, int j, uint32_t okm, const u32x4 (&pf)[2]) {
+  // O^T += V^T P^T for one tile from V ring slot `slot` (compile-time). With `clip`
+  // (only the last tile of the range), values past the sequence end read as zero:
+  // their weights are zero but the cache slots may hold anything.
+  auto pv = [&](auto slot_tag, auto clip_tag, int j, const u32x4 (&pf)[2]) {
     constexpr int slot = decltype(slot_tag)::value;
+    constexpr bool clip = decltype(clip_tag)::value;
     const unsigned char* base = smem + VBUF + slot * KT_BYTES;
     const int kt = j * KT;
-    const bool clipped = okm != 0x3u || kt + KT > kv_len;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int b = 0; b < 2; ++b) {  // 16-key block of the tile; this lane's keys 16 b + 8 hi .. +8
         u32x4 vf = *reinterpret_cast<const u32x4*>(base + v_off + b * VSUB + db * 32 * (kBlockSize * 2));
-        if (clipped) vf = ((okm >> b) & 1u) ? clip_keys(vf, kt + 16 * b + 8 * hi, kv_len) : zero4();
+        if (clip) vf = clip_keys(vf, kt + 16 * b + 8 * hi, kv_len);
         o[db] = mfma32(vf, pf[b], o[db]);
       }
   };
@@ -372,36 +377,55 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     f32x16 sa, sb;
     u32x4 pf[2];
-    qk(std::integral_constant<int, 0>{}, ids0.ok, sa);
-    uint32_t ok_j = ids0.ok, ok_j1 = ids1.ok;  // valid-block masks of tiles j, j+1
+    qk(std::integral_constant<int, 0>{}, sa);
+    // Steady step u (tile j = t0 + u, not the last): S(j) is in scur, K(j+1) in K
+    // slot (u+1)%4, V(j) in V slot u%4. Issue K(j+3) and V(j+2) (their slots were
+    // last read two steps ago), S(j+1) = QK(j+1) next to the softmax of tile j, then
+    // P(j) V(j). Every step issues the same number of tile loads, so waiting for at
+    // most that many outstanding completes everything older (in-order completion).
     auto step = [&](auto slot_tag, int u, f32x16& scur, f32x16& snext) {
       constexpr int sl = decltype(slot_tag)::value;  // u % 4
       const int j = t0 + u;
       // ids of tiles j+32 .. j+63 replace those of tiles j-32 .. j-1 (long consumed);
-      // first read (tile j+32, by step u+29) comes after two barriers
+      // the first read (tile j+32, by step u+29) comes after two barriers
       if ((u & 31) == 0 && u > 0) fill_ids(j + 32, t0);
       const Ids ik = read_ids(j + 3, t0);
       issue_k(ik, (sl + 3) & 3);
       issue_v(pending, (sl + 2) & 3);
-      const uint32_t ok_j2 = pending.ok;
       pending = ik;
-      if (u + 1 < n) qk(std::integral_constant<int, (sl + 1) & 3>{}, ok_j1, snext);
+      qk(std::integral_constant<int, (sl + 1) & 3>{}, snext);
       softmax(j, scur, pf);
-      pv(std::integral_constant<int, sl>{}, j, ok_j, pf);
-      ok_j = ok_j1;
-      ok_j1 = ok_j2;
-      // Loads issued before this step are complete (in-order completion); a bare
-      // barrier publishes them without waiting for this step's loads.
+      pv(std::integral_constant<int, sl>{}, std::false_type{}, j, pf);
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(kIssuePerStep) : "memory");
     };
-    for (int u = 0; u < n; u += 4) {
+    // The last tile: softmax and P V with the sequence-end clip, nothing to issue.
+    auto last = [&](auto slot_tag, f32x16& scur) {
+      softmax(t1 - 1, scur, pf);
+      pv(slot_tag, std::true_type{}, t1 - 1, pf);
+    };
+    int u = 0;
+    for (; u + 4 < n; u += 4) {
       step(std::integral_constant<int, 0>{}, u, sa, sb);
-      if (u + 1 >= n) break;
       step(std::integral_constant<int, 1>{}, u + 1, sb, sa);
-      if (u + 2 >= n) break;
       step(std::integral_constant<int, 2>{}, u + 2, sa, sb);
-      if (u + 3 >= n) break;
       step(std::integral_constant<int, 3>{}, u + 3, sb, sa);
+    }
+    // 1 to 4 tiles remain (u = n-4 .. n-1); S(t0+u) is in sa
+    const int rem = n - u;
+    if (rem == 1) {
+      last(std::integral_constant<int, 0>{}, sa);
+    } else if (rem == 2) {
+      step(std::integral_constant<int, 0>{}, u, sa, sb);
+      last(std::integral_constant<int, 1>{}, sb);
+    } else if (rem == 3) {
+      step(std::integral_constant<int, 0>{}, u, sa, sb);
+      step(std::integral_constant<int, 1>{}, u + 1, sb, sa);
+      last(std::integral_constant<int, 2>{}, sa);
+    } else {
+      step(std::integral_constant<int, 0>{}, u, sa, sb);
+      step(std::integral_constant<int, 1>{}, u + 1, sb, sa);
+      step(std::integral_constant<int, 2>{}, u + 2, sa, sb);
+      last(std::integral_constant<int, 3>{}, sb);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads issued past the end
   }

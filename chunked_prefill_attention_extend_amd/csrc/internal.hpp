@@ -71,6 +71,7 @@ struct AttnArgs {
   const CombineTask* tasks;
   float* slots;
   int32_t* err;
+  const void* zero_page;  // kZeroPageBytes of zeros in the workspace (stands in for invalid blocks)
   int64_t num_blocks;
   int32_t max_blocks;
   int32_t num_seqs;
@@ -109,10 +110,11 @@ struct Plan {
   int64_t n_slots = 0;
   int64_t total_rows = 0;
   // byte offsets inside the workspace
-  size_t off_seqs = 0, off_items = 0, off_tasks = 0, off_slots = 0, bytes = 0, upload_bytes = 0;
+  size_t off_zero = 0, off_seqs = 0, off_items = 0, off_tasks = 0, off_slots = 0, bytes = 0, upload_bytes = 0;
 };
 
 constexpr size_t kHeaderBytes = 256;  // error word + padding
+constexpr size_t kZeroPageBytes = size_t(kBlockSize) * 128 * 4;  // one (block, head) of the largest head_dim, fp32
 
 // plan.cpp
 int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,

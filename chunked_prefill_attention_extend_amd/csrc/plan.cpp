@@ -103,6 +103,8 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
   }
 
   size_t off = kHeaderBytes;
+  plan.off_zero = off;
+  off += kZeroPageBytes;
   plan.off_seqs = off;
   off = align_up(off + sizeof(SeqInfo) * num_seqs, 256);
   plan.off_items = off;
