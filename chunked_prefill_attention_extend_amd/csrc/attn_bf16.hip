@@ -162,8 +162,15 @@ __device__ inline void write_row(const AttnArgs& a, const f32x16 (&o)[D / 32], f
 // ---------------------------------------------------------------------------
 __device__ inline int swz_v(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
 
-// Reductions over the two lanes (l, l ^ 32) that hold one query row.
-__device__ inline float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// Value of lane l ^ 32 (the other lane holding the same query row).
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes 0..31
+// of its second; either result then holds the partner value in the lane half that
+// received it, whether or not both operands share a register.
+__device__ inline float partner(float x, int hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, hi ? r[0] : r[1]);
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -179,11 +186,12 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   constexpr int DB = D / 32;                      // 32-feature blocks of O^T
   constexpr int KT_BYTES = KT * D * 2;            // one K tile (= one V tile)
   constexpr int VSUB = D * kBlockSize * 2;        // one V^T sub-tile (16 keys)
-  constexpr int NINST = KT_BYTES / 1024 / 4;      // 1 KB direct loads per wave per tile (K and V each)
+  constexpr int PIECES = KT_BYTES / 1024;         // 1 KB direct loads per tile (K and V each)
+  constexpr int NINST = (PIECES + kWaves - 1) / kWaves;  // per wave
   constexpr int RING = 4;                         // LDS ring slots per operand
   constexpr int KBUF = 0, VBUF = RING * KT_BYTES; // LDS: K ring, then V ring, then block ids
   constexpr int IDBUF = 2 * RING * KT_BYTES;
-  static_assert(NINST >= 1, "tile too small for the workgroup");
+  static_assert(PIECES % kWaves == 0 || kWaves % PIECES == 0, "pieces must split evenly over the waves");
 
   const int tid = threadIdx.x;
   // wave index as a uniform (scalar) value: block bases and LDS destinations stay in SGPRs
@@ -235,10 +243,14 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     int32_t p0, p1;  // uniform block ids (invalid ones replaced by -1: read the zero page)
     uint32_t ok;     // valid-block mask
   };
+  // The ids of a 32-tile window (64 entries) sit one per lane in `idwin`, loaded
+  // from the ring once per window; a tile's two ids are then picked with readlane.
+  int32_t idwin = 0;
+  auto load_window = [&](int k) { idwin = id_ring[(k & 1) * 64 + lane]; };
   auto read_ids = [&](int j, int t0_) -> Ids {
-    const int e = ((j - t0_) & 63) * 2;
-    int32_t v0 = __builtin_amdgcn_readfirstlane(id_ring[e]);
-    int32_t v1 = __builtin_amdgcn_readfirstlane(id_ring[e + 1]);
+    const int e = ((j - t0_) & 31) * 2;
+    int32_t v0 = __builtin_amdgcn_readlane(idwin, e);
+    int32_t v1 = __builtin_amdgcn_readlane(idwin, e + 1);
     if (j * 2 >= nblk) v0 = -1;
     if (j * 2 + 1 >= nblk) v1 = -1;
     const bool ok0 = block_ok(v0, a.num_blocks), ok1 = block_ok(v1, a.num_blocks);
@@ -248,36 +260,42 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     }
     return Ids{ok0 ? v0 : -1, ok1 ? v1 : -1, uint32_t(ok0) | (uint32_t(ok1) << 1)};
   };
-  // Direct loads of one tile: waves 0, 1 load block 0 of the tile, waves 2, 3 block 1;
-  // each wave copies half of its block's K (rows) and half of its V (feature rows).
-  // Source of this wave's block: the cache, or the zero page for an invalid id.
-  auto block_base = [&](const uint16_t* cache, const Ids& ids) -> const unsigned char* {
-    const int32_t blk = wave < 2 ? ids.p0 : ids.p1;
+  // Piece i (1 KB) of a tile lies in block i / (PIECES / 2) of the tile for both K
+  // (rows of D elements) and V (sub-tiles of D x 16); wave w loads pieces w + kWaves x.
+  auto block_base = [&](const uint16_t* cache, const Ids& ids, int piece) -> const unsigned char* {
+    const int32_t blk = piece < PIECES / 2 ? ids.p0 : ids.p1;
     return blk < 0 ? static_cast<const unsigned char*>(a.zero_page)
                    : reinterpret_cast<const unsigned char*>(cache + (int64_t(blk) * a.hkv + g) * (kBlockSize * D));
   };
+  // Per-lane byte offsets (within the piece's block) of this wave's direct loads.
+  uint32_t k_src[NINST], v_src[NINST];
+#pragma unroll
+  for (int x = 0; x < NINST; ++x) {
+    const int i = wave + kWaves * x;  // 1 KB piece of the tile
+    // K: 16-byte slot (i, lane) is row r (key r of the tile), position c; it holds piece c ^ swz_k(r)
+    const int n = i * 64 + lane;
+    const int r = n / NC, c = n % NC;
+    k_src[x] = uint32_t(((r & 15) * D + ((c ^ (key_of_row(r & 15) & (NC - 1))) * 8)) * 2);
+    // V: slot (i, lane) is feature row d of sub-tile i / (PIECES / 2), position cv; it holds half cv ^ swz_v(d)
+    const int d = ((i * 64 + lane) % (VSUB / 16)) / 2, cv = lane & 1;
+    v_src[x] = uint32_t((d * kBlockSize + ((cv ^ swz_v(d)) * 8)) * 2);
+  }
   auto issue_k = [&](const Ids& ids, int slot) {
     unsigned char* dst = smem + KBUF + slot * KT_BYTES;
-    const unsigned char* base = block_base(kc, ids);
 #pragma unroll
     for (int x = 0; x < NINST; ++x) {
-      const int i = wave * NINST + x;  // 1 KB piece of the tile
-      const int n = i * 64 + lane;     // 16-byte slot: row r (key), position c
-      const int r = n / NC, c = n % NC;
-      const uint32_t off = uint32_t(((r & 15) * D + ((c ^ (key_of_row(r & 15) & (NC - 1))) * 8)) * 2);
-      __builtin_amdgcn_global_load_lds(base + off, (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
+      const int i = wave + kWaves * x;
+      if (i < PIECES)
+        __builtin_amdgcn_global_load_lds(block_base(kc, ids, i) + k_src[x], (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
     }
   };
   auto issue_v = [&](const Ids& ids, int slot) {
     unsigned char* dst = smem + VBUF + slot * KT_BYTES;
-    const unsigned char* base = block_base(vc, ids);
 #pragma unroll
     for (int x = 0; x < NINST; ++x) {
-      const int i = wave * NINST + x;                          // 1 KB piece of the tile
-      const int d = ((i * 64 + lane) % (VSUB / 16)) / 2;       // feature row within the sub-tile
-      const int cv = lane & 1;                                 // position; holds half cv ^ swz_v(d)
-      const uint32_t off = uint32_t((d * kBlockSize + ((cv ^ swz_v(d)) * 8)) * 2);
-      __builtin_amdgcn_global_load_lds(base + off, (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
+      const int i = wave + kWaves * x;
+      if (i < PIECES)
+        __builtin_amdgcn_global_load_lds(block_base(vc, ids, i) + v_src[x], (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
     }
   };
 
@@ -298,18 +316,26 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       s = mfma32(kf, qf[ks], s);
     }
   };
-  // Online softmax of one tile: mask, lazy max update, weights as packed bf16.
-  auto softmax = [&](int j, f32x16& s, u32x4 (&pf)[2]) {
+  // Online softmax of one tile, in three parts so that each can sit next to MFMA work:
+  //   row_max: this lane's max of the raw scores (no masking);
+  //   settle:  mask a diagonal or end tile (then re-take the max), exchange with the
+  //            partner lane, raise the running max m lazily (rescaling O and l);
+  //   weights: p = 2^(s c - m) as packed bf16 for the P.V product, and the row sum.
+  auto row_max = [&](const f32x16& s) -> float {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    return mx;
+  };
+  auto settle = [&](int j, f32x16& s, float mx) {
     const int kt = j * KT;
     if (kt + KT - 1 > lim_min) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (kt + key_of_elem(i, hi) > lim) s[i] = -INFINITY;
+      mx = row_max(s);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = pair_max(mx) * c2;
+    mx = fmaxf(mx, partner(mx, hi)) * c2;
     // wave-uniform decision; every lane then moves m to its exact new max
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
       const float mnew = fmaxf(m, mx);
@@ -319,6 +345,8 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       l *= alpha;
       m = mnew;
     }
+  };
+  auto weights = [&](const f32x16& s, u32x4 (&pf)[2]) {
     const float msafe = (m == -INFINITY) ? 0.f : m;
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -361,11 +389,13 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     // two steps earlier). Every step issues the same number of vector memory
     // instructions (ids and tiles past the end load harmless entries), so waiting
     // for "at most one step's worth outstanding" completes everything older.
-    constexpr int kIssuePerStep = 2 * NINST;  // tile loads per step (the id refills come on top)
+    // tile loads per step and wave (the id refills come on top); waves without a piece issue none
+    constexpr int kIssuePerStep = 2 * NINST;
     // Prologue: ids of tiles t0 .. t0+63, then K and V of t0 and t0+1, K of t0+2.
     fill_ids(t0, t0);
     fill_ids(t0 + 32, t0);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    load_window(0);
     const Ids ids0 = read_ids(t0, t0);
     issue_k(ids0, 0);
     issue_v(ids0, 0);
@@ -378,29 +408,54 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     f32x16 sa, sb;
     u32x4 pf[2];
     qk(std::integral_constant<int, 0>{}, sa);
-    // Steady step u (tile j = t0 + u, not the last): S(j) is in scur, K(j+1) in K
-    // slot (u+1)%4, V(j) in V slot u%4. Issue K(j+3) and V(j+2) (their slots were
-    // last read two steps ago), S(j+1) = QK(j+1) next to the softmax of tile j, then
-    // P(j) V(j). Every step issues the same number of tile loads, so waiting for at
-    // most that many outstanding completes everything older (in-order completion).
+    settle(t0, sa, row_max(sa));
+    // Steady step u (tile j = t0 + u, not the last): S(j) is in scur with m settled,
+    // K(j+1) in K slot (u+1)%4, V(j) in V slot u%4. Issue K(j+3) and V(j+2) (their
+    // slots were last read two steps ago); then
+    //   region A: S(j+1) = QK(j+1) MFMAs interleaved with tile j's weights,
+    //   region B: O += P(j) V(j) MFMAs interleaved with tile j+1's row max,
+    // then settle tile j+1. Every step issues the same number of tile loads, so
+    // waiting for at most that many outstanding completes everything older.
     auto step = [&](auto slot_tag, int u, f32x16& scur, f32x16& snext) {
       constexpr int sl = decltype(slot_tag)::value;  // u % 4
       const int j = t0 + u;
       // ids of tiles j+32 .. j+63 replace those of tiles j-32 .. j-1 (long consumed);
       // the first read (tile j+32, by step u+29) comes after two barriers
       if ((u & 31) == 0 && u > 0) fill_ids(j + 32, t0);
+      if (((u + 3) & 31) == 0) load_window((u + 3) >> 5);  // tile j+3 starts a new window
       const Ids ik = read_ids(j + 3, t0);
       issue_k(ik, (sl + 3) & 3);
       issue_v(pending, (sl + 2) & 3);
       pending = ik;
+      __builtin_amdgcn_sched_barrier(0);  // regions A and B are scheduled separately
+      // region A
       qk(std::integral_constant<int, (sl + 1) & 3>{}, snext);
-      softmax(j, scur, pf);
+      weights(scur, pf);
+      // keep the K operand reads 3 ahead of the MFMAs that use them
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS read
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);  // VALU incl. exp
+        if (i + 3 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // region B
       pv(std::integral_constant<int, sl>{}, std::false_type{}, j, pf);
+      const float mx = row_max(snext);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);  // LDS read
+#pragma unroll
+      for (int i = 0; i < 2 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, 1, 1);  // VALU
+        if (i + 3 < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
+      }
+      settle(j + 1, snext, mx);
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(kIssuePerStep) : "memory");
     };
-    // The last tile: softmax and P V with the sequence-end clip, nothing to issue.
+    // The last tile: weights and P V with the sequence-end clip, nothing to issue.
     auto last = [&](auto slot_tag, f32x16& scur) {
-      softmax(t1 - 1, scur, pf);
+      weights(scur, pf);
       pv(slot_tag, std::true_type{}, t1 - 1, pf);
     };
     int u = 0;
@@ -567,7 +622,7 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it) {
   };
 
   const int nt = (it.key_end - it.key_begin + kSplitTile - 1) / kSplitTile;
-  const int tw0 = wave * nt / 4, tw1 = (wave + 1) * nt / 4;
+  const int tw0 = wave * nt / kWaves, tw1 = (wave + 1) * nt / kWaves;
   Tile ta, tb;
   if (tw0 < tw1) load(tw0, ta);
   for (int jj = tw0; jj < tw1; jj += 2) {

@@ -10,12 +10,13 @@
 namespace extattn {
 
 constexpr int kBlockSize = 16;    // tokens per paged-cache block
-constexpr int kThreads = 256;     // 4 wave64 per workgroup
+constexpr int kWaves = 8;         // wave64 per workgroup
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;  // query rows per wave (one 32x32 MFMA column block)
-constexpr int kRowsPerTile = 128; // chunk path: 4 waves x 32 rows share each K/V tile
+constexpr int kRowsPerTile = kWaves * 32;  // chunk path: all waves' rows share each K/V tile
 constexpr int kChunkKeys = 32;    // chunk path: keys per LDS K/V tile (one 32x32 S^T block)
 constexpr int kSplitTile = 32;    // split path: keys per register K/V tile
-constexpr int kSplitKeys = 1024;  // split path: keys per workgroup (4 waves)
+constexpr int kSplitKeys = 2048;  // split path: keys per workgroup (kWaves waves)
 constexpr int kSplitRows = 16;    // split path: at most this many rows (one 16-row MFMA block)
 
 // Per-request metadata copied to the workspace.
@@ -27,8 +28,8 @@ struct SeqInfo {
 };
 
 enum : int32_t {
-  kItemChunk = 0,  // 128 rows of one (request, KV head); 4 waves share LDS K/V tiles
-  kItemSplit = 1,  // <= 16 rows; each of the 4 waves takes its own part of the key range
+  kItemChunk = 0,  // kRowsPerTile rows of one (request, KV head); all waves share LDS K/V tiles
+  kItemSplit = 1,  // <= 16 rows; each wave takes its own part of the key range
 };
 
 // One workgroup's work. Rows are flattened per (request, KV head) as
@@ -38,7 +39,7 @@ struct WorkItem {
   int32_t seq;
   int32_t kv_head;
   int32_t row0;       // first flattened row
-  int32_t nrows;      // rows in this item (<= 128 chunk, <= 32 split)
+  int32_t nrows;      // rows in this item (<= kRowsPerTile chunk, <= kSplitRows split)
   int32_t key_begin;  // keys [key_begin, key_end); key_begin is a multiple of 64
   int32_t key_end;
   int32_t slot;       // < 0: write out/lse directly; else first partial slot (one per wave)

@@ -42,9 +42,9 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Work list of one launch. Requests whose E * group rows fit one 16-row MFMA
 // block (decode rows, short verify rows) take the split path: the key range is cut into
-// kSplitKeys pieces, each piece into four per-wave parts, and the partial
+// kSplitKeys pieces, each piece into one part per wave, and the partial
 // results are merged by the combine kernel. Longer chunks take the chunk path:
-// 128-row tiles over their whole causal key range.
+// kRowsPerTile-row tiles over their whole causal key range.
 int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
                int32_t head_dim, int32_t dtype, Plan& plan) {
   const int32_t group = hq / hkv;
@@ -72,10 +72,10 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
             const int64_t kb = w * kSplitKeys;
             const int64_t ke = std::min<int64_t>(kv_len, kb + kSplitKeys);
             split_items.push_back(WorkItem{kItemSplit, r, g, 0, int32_t(rows), int32_t(kb), int32_t(ke),
-                                           int32_t(slot0 + 4 * w)});
+                                           int32_t(slot0 + kWaves * w)});
           }
-          plan.tasks.push_back(CombineTask{r, g, 0, int32_t(rows), int32_t(slot0), int32_t(4 * nwg), 1, 0});
-          plan.n_slots += 4 * nwg;
+          plan.tasks.push_back(CombineTask{r, g, 0, int32_t(rows), int32_t(slot0), int32_t(kWaves * nwg), 1, 0});
+          plan.n_slots += kWaves * nwg;
         }
       } else {
         const int64_t ntiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
