@@ -211,6 +211,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--only-mixed", action="store_true", help="run only the mixed-step measurement (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 launches), the reference for HBM byte counters")
     args = ap.parse_args()
@@ -235,6 +236,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n, "bytes_written_per_launch": n,
                                                "launches": 3}}), flush=True)
+        return 0
+    if args.only_mixed:
+        print(json.dumps({"mixed_step": mixed_step_bench(torch, ext, synth)}), flush=True)
         return 0
     log("setting up the 128-chunk sweep")
     s = setup_sweep(torch, ext, synth)

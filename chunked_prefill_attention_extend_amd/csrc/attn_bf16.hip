@@ -504,7 +504,7 @@ __device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 template <int D>
-__device__ void split_item(const AttnArgs& a, const WorkItem& it) {
+__device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char* smem) {
   constexpr int KS = D / 32;  // 32-wide k-steps over the head dim
   constexpr int DB = D / 16;  // 16-feature blocks of O^T
   const int tid = threadIdx.x;
@@ -634,29 +634,82 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it) {
     }
   }
 
-  // Partial result of this wave: normalised o (fp32) and natural-log lse.
+  // Merge the waves' partial results through LDS (the page's merge rule over the
+  // kWaves parts): part[w][row][d] holds unnormalised o, mls[w][row] = (m, l).
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
-  if (!valid) return;
-  float* sl = a.slots + size_t(it.slot + wave) * slot_floats(D);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  float* part = reinterpret_cast<float*>(smem);
+  float* mls = part + kWaves * kSplitRows * D;
+  if (valid) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    float4 v = {o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
-    *reinterpret_cast<float4*>(sl + l16 * D + db * 16 + 4 * q4) = v;
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<float4*>(part + (wave * kSplitRows + l16) * D + db * 16 + 4 * q4) =
+          float4{o[db][0], o[db][1], o[db][2], o[db][3]};
+    if (q4 == 0) {
+      mls[(wave * kSplitRows + l16) * 2] = m;
+      mls[(wave * kSplitRows + l16) * 2 + 1] = lt;
+    }
   }
-  if (q4 == 0) sl[kRowsPerWave * D + l16] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+  __syncthreads();
+  constexpr int TPR = D / 4;  // threads per row, 4 features each
+  static_assert(kThreads / TPR >= kSplitRows, "one pass must cover the rows");
+  const int r = tid / TPR, c4 = (tid % TPR) * 4;
+  const bool act = r < it.nrows;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f, M = -INFINITY;
+  if (act) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mls[(w * kSplitRows + r) * 2]);
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float lw = mls[(w * kSplitRows + r) * 2 + 1];
+        if (lw > 0.f) {
+          const float f = __builtin_amdgcn_exp2f(mls[(w * kSplitRows + r) * 2] - M);
+          const float4 ow = *reinterpret_cast<const float4*>(part + (w * kSplitRows + r) * D + c4);
+          L += f * lw;
+          acc.x += f * ow.x;
+          acc.y += f * ow.y;
+          acc.z += f * ow.z;
+          acc.w += f * ow.w;
+        }
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float lse_wg = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+  const int rpos = act ? r / G : 0;
+  const int64_t orow_r = int64_t(si.q_off + rpos) * a.hq + g * G + (act ? r - rpos * G : 0);
+  auto store_out = [&](float4 v, float lse_v) {
+    uint16_t* op = static_cast<uint16_t*>(a.out) + orow_r * D + c4;
+    u32x2 pk = {pack2(v.x, v.y), pack2(v.z, v.w)};
+    *reinterpret_cast<u32x2*>(op) = pk;
+    if (c4 == 0 && a.lse) a.lse[orow_r] = lse_v;
+  };
+  if (it.task < 0) {  // this workgroup covered the whole key range
+    if (act) store_out(float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv}, lse_wg);
+    return;
+  }
+  // Leave this workgroup's partial (normalised o, natural-log lse) in its slot; the
+  // combine kernel merges the workgroups' partials of the task.
+  float* sl = a.slots + size_t(it.slot) * slot_floats(D);
+  if (act) {
+    *reinterpret_cast<float4*>(sl + r * D + c4) = float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    if (c4 == 0) sl[kRowsPerWave * D + r] = lse_wg;
+  }
 }
 
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 4 * kChunkKeys * D * 2 + 512];
+  constexpr int kChunkLds = 2 * 4 * kChunkKeys * D * 2 + 512;                     // K/V rings + block ids
+  constexpr int kSplitLds = kWaves * kSplitRows * (D + 2) * 4;                     // wave partials
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kChunkLds > kSplitLds ? kChunkLds : kSplitLds];
   const WorkItem it = a.items[blockIdx.x];
   if (it.kind == kItemChunk)
     chunk_item<D>(a, it, smem);
   else
-    split_item<D>(a, it);
+    split_item<D>(a, it, smem);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {

@@ -42,7 +42,9 @@ struct WorkItem {
   int32_t nrows;      // rows in this item (<= kRowsPerTile chunk, <= kSplitRows split)
   int32_t key_begin;  // keys [key_begin, key_end); key_begin is a multiple of 64
   int32_t key_end;
-  int32_t slot;       // < 0: write out/lse directly; else first partial slot (one per wave)
+  int32_t slot;       // < 0: write out/lse directly; else the partial slot (chunk: one per wave, split: one)
+  int32_t task;       // split items: combine task that merges this workgroup's slot, or -1 (direct write)
+  int32_t pad[3];
 };
 
 // Merge of partial results for <= 32 rows of one (request, KV head).

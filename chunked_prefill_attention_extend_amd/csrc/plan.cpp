@@ -42,8 +42,9 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Work list of one launch. Requests whose E * group rows fit one 16-row MFMA
 // block (decode rows, short verify rows) take the split path: the key range is cut into
-// kSplitKeys pieces, each piece into one part per wave, and the partial
-// results are merged by the combine kernel. Longer chunks take the chunk path:
+// kSplitKeys pieces (one workgroup each, one part per wave); each workgroup
+// merges its waves' parts and leaves one partial result, and the combine kernel
+// merges the workgroups' partials. Longer chunks take the chunk path:
 // kRowsPerTile-row tiles over their whole causal key range.
 int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
                int32_t head_dim, int32_t dtype, Plan& plan) {
@@ -67,15 +68,18 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
       if (rows <= kSplitRows) {
         const int64_t nwg = (kv_len + kSplitKeys - 1) / kSplitKeys;
         for (int32_t g = 0; g < hkv; ++g) {
-          const int64_t slot0 = plan.n_slots;
+          const int64_t slot0 = nwg > 1 ? plan.n_slots : -1;
+          const int32_t task = nwg > 1 ? int32_t(plan.tasks.size()) : -1;
           for (int64_t w = 0; w < nwg; ++w) {
             const int64_t kb = w * kSplitKeys;
             const int64_t ke = std::min<int64_t>(kv_len, kb + kSplitKeys);
             split_items.push_back(WorkItem{kItemSplit, r, g, 0, int32_t(rows), int32_t(kb), int32_t(ke),
-                                           int32_t(slot0 + kWaves * w)});
+                                           int32_t(nwg > 1 ? slot0 + w : -1), task, {0, 0, 0}});
           }
-          plan.tasks.push_back(CombineTask{r, g, 0, int32_t(rows), int32_t(slot0), int32_t(kWaves * nwg), 1, 0});
-          plan.n_slots += kWaves * nwg;
+          if (nwg > 1) {
+            plan.tasks.push_back(CombineTask{r, g, 0, int32_t(rows), int32_t(slot0), int32_t(nwg), 1, 0});
+            plan.n_slots += nwg;
+          }
         }
       } else {
         const int64_t ntiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
@@ -86,7 +90,7 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
             const int64_t pos_max = (row0 + nrows - 1) / group;
             const int64_t key_end = int64_t(prefix[r]) + pos_max + 1;
             chunk_items.push_back(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), 0,
-                                           int32_t(key_end), -1});
+                                           int32_t(key_end), -1, -1, {0, 0, 0}});
           }
         }
       }
