@@ -169,14 +169,35 @@ __device__ inline int swz_v(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
 __device__ inline float partner(float x, int hi) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
                                                   false, false);
-  return __builtin_bit_cast(float, hi ? r[0] : r[1]);
+  const uint32_t v = hi ? r[0] : r[1];
+  return __builtin_bit_cast(float, v);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Lazy rescale threshold (log2 units): the running max m is raised only when a
-// tile's max exceeds it by more than this, so softmax weights stay <= 2^8.
-constexpr float kRescaleSlack = 8.0f;
+// LDS byte address of a pointer into the workgroup's shared memory, as a wave-uniform value.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p)));
+}
+
+// Direct copies from global memory into LDS: lane l's 16 (or 4) bytes at base + off
+// land at LDS address lds + 16 l (4 l). They are issued as inline assembly on purpose:
+// the compiler's wait-count pass treats any direct-to-LDS load it sees as a possible
+// producer of every later LDS read and then drains all LDS reads before each use
+// (s_waitcnt lgkmcnt(0)), which serialises the MFMA operand reads. The kernel orders
+// these copies itself (s_waitcnt vmcnt and a barrier before the data is read); loads
+// the compiler does not know about only make its own vmcnt waits stricter.
+__device__ inline void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
+}
+__device__ inline void dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
+}
+
+// Bound on one lane's row sum of a chunk tile's 16 weights. Below it every weight is
+// at most 2^12, so O and l stay far from fp32 overflow; above it (or when a weight
+// overflowed to inf) the running max is raised before the weights are used.
+constexpr float kSumBound = 4096.0f;
 
 template <int D>
 __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char* smem) {
@@ -228,42 +249,42 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   const int k_off0 = key_of_row(l32) * (D * 2) + (((hi ^ (l32 & 15)) & (NC - 1)) << 4);
   const int v_off = l32 * (kBlockSize * 2) + ((hi ^ swz_v(l32)) << 4);
 
+  const int t0 = it.key_begin / KT;
+  const int t1 = (it.key_end + KT - 1) / KT;
+  const int n = t1 - t0;
+
   // Block ids go through a small LDS ring (64 tiles = 128 ids) filled by direct
   // loads, 32 tiles at a time, so the loop holds no register-destination loads.
   int32_t* id_ring = reinterpret_cast<int32_t*>(smem + IDBUF);
   // Copy the ids of tiles [jt, jt + 32) into ring half (jt - t0) / 32 % 2 (wave 0 only).
-  auto fill_ids = [&](int jt, int t0_) {
+  auto fill_ids = [&](int jt) {
     if (wave != 0) return;
     const int lb = jt * (KT / kBlockSize) + lane;  // 64 ids
     const int src = lb < nblk ? lb : nblk - 1;     // stay inside the table row
-    const int half = ((jt - t0_) / 32) & 1;
-    __builtin_amdgcn_global_load_lds(bt + src, (lds_ptr_t)(id_ring + half * 64), 4, 0, 0);
+    const int half = ((jt - t0) / 32) & 1;
+    dma4(bt, uint32_t(src) * 4u, lds_addr(id_ring + half * 64));
   };
-  struct Ids {
-    int32_t p0, p1;  // uniform block ids (invalid ones replaced by -1: read the zero page)
-    uint32_t ok;     // valid-block mask
+  // Each wave copies one 1 KB piece of every K and V tile (waves beyond the piece
+  // count copy nothing); piece `wave` lies in block my_blk of the tile.
+  static_assert(NINST == 1, "one piece per wave and tile");
+  const bool has_piece = wave < PIECES;
+  const int my_blk = has_piece ? wave / (PIECES / 2) : 0;
+  // The ids of a 32-tile window (64 entries) sit one per lane in `idwin`, loaded from
+  // the ring once per window and checked there: entries past the sequence end and
+  // ids outside [0, num_blocks) become -1 (read the zero page); the invalid ones are
+  // counted in the error word (once per window and workgroup).
+  int32_t idwin = -1;
+  auto load_window = [&](int k) {
+    const int32_t v = id_ring[(k & 1) * 64 + lane];
+    const bool inside = (t0 + 32 * k) * (KT / kBlockSize) + lane < nblk;
+    const bool ok = block_ok(v, a.num_blocks);
+    const uint64_t bad = __builtin_amdgcn_ballot_w64(inside && !ok);
+    if (bad != 0 && wave == 0 && lane == 0) atomicAdd(a.err, int(__builtin_popcountll(bad)));
+    idwin = (inside && ok) ? v : -1;
   };
-  // The ids of a 32-tile window (64 entries) sit one per lane in `idwin`, loaded
-  // from the ring once per window; a tile's two ids are then picked with readlane.
-  int32_t idwin = 0;
-  auto load_window = [&](int k) { idwin = id_ring[(k & 1) * 64 + lane]; };
-  auto read_ids = [&](int j, int t0_) -> Ids {
-    const int e = ((j - t0_) & 31) * 2;
-    int32_t v0 = __builtin_amdgcn_readlane(idwin, e);
-    int32_t v1 = __builtin_amdgcn_readlane(idwin, e + 1);
-    if (j * 2 >= nblk) v0 = -1;
-    if (j * 2 + 1 >= nblk) v1 = -1;
-    const bool ok0 = block_ok(v0, a.num_blocks), ok1 = block_ok(v1, a.num_blocks);
-    if (tid == 0) {
-      if (!ok0 && j * 2 < nblk) atomicAdd(a.err, 1);
-      if (!ok1 && j * 2 + 1 < nblk) atomicAdd(a.err, 1);
-    }
-    return Ids{ok0 ? v0 : -1, ok1 ? v1 : -1, uint32_t(ok0) | (uint32_t(ok1) << 1)};
-  };
-  // Piece i (1 KB) of a tile lies in block i / (PIECES / 2) of the tile for both K
-  // (rows of D elements) and V (sub-tiles of D x 16); wave w loads pieces w + kWaves x.
-  auto block_base = [&](const uint16_t* cache, const Ids& ids, int piece) -> const unsigned char* {
-    const int32_t blk = piece < PIECES / 2 ? ids.p0 : ids.p1;
+  // This wave's block id of tile j (wave-uniform).
+  auto read_blk = [&](int j) -> int32_t { return __builtin_amdgcn_readlane(idwin, ((j - t0) & 31) * 2 + my_blk); };
+  auto block_base = [&](const uint16_t* cache, int32_t blk) -> const unsigned char* {
     return blk < 0 ? static_cast<const unsigned char*>(a.zero_page)
                    : reinterpret_cast<const unsigned char*>(cache + (int64_t(blk) * a.hkv + g) * (kBlockSize * D));
   };
@@ -280,29 +301,20 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     const int d = ((i * 64 + lane) % (VSUB / 16)) / 2, cv = lane & 1;
     v_src[x] = uint32_t((d * kBlockSize + ((cv ^ swz_v(d)) * 8)) * 2);
   }
-  auto issue_k = [&](const Ids& ids, int slot) {
-    unsigned char* dst = smem + KBUF + slot * KT_BYTES;
-#pragma unroll
-    for (int x = 0; x < NINST; ++x) {
-      const int i = wave + kWaves * x;
-      if (i < PIECES)
-        __builtin_amdgcn_global_load_lds(block_base(kc, ids, i) + k_src[x], (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
-    }
+  auto issue_k = [&](int32_t blk, int slot) {
+    if (has_piece) dma16(block_base(kc, blk), k_src[0], lds_addr(smem + KBUF + slot * KT_BYTES + wave * 1024));
   };
-  auto issue_v = [&](const Ids& ids, int slot) {
-    unsigned char* dst = smem + VBUF + slot * KT_BYTES;
-#pragma unroll
-    for (int x = 0; x < NINST; ++x) {
-      const int i = wave + kWaves * x;
-      if (i < PIECES)
-        __builtin_amdgcn_global_load_lds(block_base(vc, ids, i) + v_src[x], (lds_ptr_t)(dst + i * 1024), 16, 0, 0);
-    }
+  auto issue_v = [&](int32_t blk, int slot) {
+    if (has_piece) dma16(block_base(vc, blk), v_src[0], lds_addr(smem + VBUF + slot * KT_BYTES + wave * 1024));
   };
 
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  // Running max m (log2 units of the scaled scores) and this lane's share of the row
+  // sum l. m is the exact row max of the first tile; afterwards it is raised only
+  // when a tile's weights grow past kSumBound (rare), so no tile needs a row max.
+  float m = 0.f, l = 0.f;
 
   // S^T of one tile from K ring slot `slot` (compile-time). Invalid blocks were
   // loaded from the zero page; keys past the sequence end are masked later.
@@ -316,50 +328,60 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       s = mfma32(kf, qf[ks], s);
     }
   };
-  // Online softmax of one tile, in three parts so that each can sit next to MFMA work:
-  //   row_max: this lane's max of the raw scores (no masking);
-  //   settle:  mask a diagonal or end tile (then re-take the max), exchange with the
-  //            partner lane, raise the running max m lazily (rescaling O and l);
-  //   weights: p = 2^(s c - m) as packed bf16 for the P.V product, and the row sum.
   auto row_max = [&](const f32x16& s) -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
     return mx;
   };
-  auto settle = [&](int j, f32x16& s, float mx) {
+  // Causal mask of a diagonal tile (and of keys past the range end). Element i holds
+  // key kt + 8 hi + key_of_elem(i, 0), so the test is one threshold against constants.
+  auto mask = [&](int j, f32x16& s) {
     const int kt = j * KT;
     if (kt + KT - 1 > lim_min) {
+      const int t = lim - kt - 8 * hi;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (kt + key_of_elem(i, hi) > lim) s[i] = -INFINITY;
-      mx = row_max(s);
-    }
-    mx = fmaxf(mx, partner(mx, hi)) * c2;
-    // wave-uniform decision; every lane then moves m to its exact new max
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
-      const float mnew = fmaxf(m, mx);
-      const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      l *= alpha;
-      m = mnew;
+        if (key_of_elem(i, 0) > t) s[i] = -INFINITY;
     }
   };
-  auto weights = [&](const f32x16& s, u32x4 (&pf)[2]) {
-    const float msafe = (m == -INFINITY) ? 0.f : m;
-    float ls0 = 0.f, ls1 = 0.f;
+  // Weights p = 2^(s c - m) as packed bf16 for the P.V product, and this lane's sum
+  // of them over the tile. The sum adds the same bf16 values (a dot product with
+  // ones), so the normalisation matches the numerator of P.V exactly.
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto weights = [&](const f32x16& s, u32x4 (&pf)[2], float& ls) {
+    float l0 = 0.f, l1 = 0.f;
 #pragma unroll
     for (int v = 0; v < 2; ++v)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * v + 2 * w], c2, -msafe));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * v + 2 * w + 1], c2, -msafe));
-        pf[v][w] = pack2(p0, p1);
-        ls0 += p0;
-        ls1 += p1;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * v + 2 * w], c2, -m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * v + 2 * w + 1], c2, -m));
+        // (the packed value goes through a local: a bit cast of a vector element
+        // lvalue such as pf[v][w] has been seen to read element 0)
+        const uint32_t pk = pack2(p0, p1);
+        pf[v][w] = pk;
+        if (w & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l1, false);
+        else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l0, false);
       }
-    l += ls0 + ls1;
+    ls = l0 + l1;
+  };
+  // Check of a tile's weights before they enter P.V: when some lane's sum passed
+  // kSumBound (or overflowed), raise m to the rows' exact max over the tile, rescale
+  // O and l, and redo the weights. Then add the tile's sum to l.
+  auto check = [&](const f32x16& s, u32x4 (&pf)[2], float& ls) {
+    if (__builtin_amdgcn_ballot_w64(ls > kSumBound) != 0) {
+      float mx = row_max(s) * c2;
+      mx = fmaxf(mx, partner(mx, hi));
+      const float d = fmaxf(mx - m, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-d);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      l *= alpha;
+      m += d;
+      weights(s, pf, ls);
+    }
+    l += ls;
   };
   // O^T += V^T P^T for one tile from V ring slot `slot` (compile-time). With `clip`
   // (only the last tile of the range), values past the sequence end read as zero:
@@ -379,83 +401,104 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       }
   };
 
-  const int t0 = it.key_begin / KT;
-  const int t1 = (it.key_end + KT - 1) / KT;
-  const int n = t1 - t0;
   if (n > 0) {
     // Pipeline over tiles j = t0 + u: tile j's K sits in K slot u % 4 and its V in
-    // V slot u % 4. Step u computes S(j+1) = QK(j+1) next to the softmax of tile j,
-    // then P(j) V(j); it first issues K(j+3) and V(j+2) (their slots were last read
-    // two steps earlier). Every step issues the same number of vector memory
-    // instructions (ids and tiles past the end load harmless entries), so waiting
-    // for "at most one step's worth outstanding" completes everything older.
-    // tile loads per step and wave (the id refills come on top); waves without a piece issue none
+    // V slot u % 4. Every step issues the same number of tile loads (tiles past the
+    // end load the zero page), so waiting for "at most one step's worth outstanding"
+    // completes everything older; waves without a piece issue none.
     constexpr int kIssuePerStep = 2 * NINST;
     // Prologue: ids of tiles t0 .. t0+63, then K and V of t0 and t0+1, K of t0+2.
-    fill_ids(t0, t0);
-    fill_ids(t0 + 32, t0);
+    fill_ids(t0);
+    fill_ids(t0 + 32);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     load_window(0);
-    const Ids ids0 = read_ids(t0, t0);
-    issue_k(ids0, 0);
-    issue_v(ids0, 0);
-    const Ids ids1 = read_ids(t0 + 1, t0);
-    issue_k(ids1, 1);
-    issue_v(ids1, 1);
-    Ids pending = read_ids(t0 + 2, t0);  // tile j+2: K issued, V not yet
+    const int32_t b0 = read_blk(t0);
+    issue_k(b0, 0);
+    issue_v(b0, 0);
+    const int32_t b1 = read_blk(t0 + 1);
+    issue_k(b1, 1);
+    issue_v(b1, 1);
+    int32_t pending = read_blk(t0 + 2);  // tile j+2: K issued, V not yet
     issue_k(pending, 2);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     f32x16 sa, sb;
     u32x4 pf[2];
+    float ls;
+    // The first tile sets m to the rows' exact max (0 for rows with no visible key).
     qk(std::integral_constant<int, 0>{}, sa);
-    settle(t0, sa, row_max(sa));
-    // Steady step u (tile j = t0 + u, not the last): S(j) is in scur with m settled,
-    // K(j+1) in K slot (u+1)%4, V(j) in V slot u%4. Issue K(j+3) and V(j+2) (their
-    // slots were last read two steps ago); then
+    mask(t0, sa);
+    {
+      float mx = row_max(sa) * c2;
+      mx = fmaxf(mx, partner(mx, hi));
+      m = (mx == -INFINITY) ? 0.f : mx;
+    }
+    // Steady step u (tile j = t0 + u, not the last): S(j) is in scur (masked), K(j+1)
+    // in K slot (u+1)%4, V(j) in V slot u%4. Issue K(j+3) and V(j+2) (their slots
+    // were last read two steps ago); then
     //   region A: S(j+1) = QK(j+1) MFMAs interleaved with tile j's weights,
-    //   region B: O += P(j) V(j) MFMAs interleaved with tile j+1's row max,
-    // then settle tile j+1. Every step issues the same number of tile loads, so
-    // waiting for at most that many outstanding completes everything older.
+    //   check tile j's weights (rare path: raise m),
+    //   region B: O += P(j) V(j) MFMAs,
+    // then mask tile j+1 if it is a diagonal tile.
     auto step = [&](auto slot_tag, int u, f32x16& scur, f32x16& snext) {
       constexpr int sl = decltype(slot_tag)::value;  // u % 4
       const int j = t0 + u;
       // ids of tiles j+32 .. j+63 replace those of tiles j-32 .. j-1 (long consumed);
       // the first read (tile j+32, by step u+29) comes after two barriers
-      if ((u & 31) == 0 && u > 0) fill_ids(j + 32, t0);
+      if ((u & 31) == 0 && u > 0) fill_ids(j + 32);
       if (((u + 3) & 31) == 0) load_window((u + 3) >> 5);  // tile j+3 starts a new window
-      const Ids ik = read_ids(j + 3, t0);
-      issue_k(ik, (sl + 3) & 3);
+      const int32_t bk = read_blk(j + 3);
+      issue_k(bk, (sl + 3) & 3);
       issue_v(pending, (sl + 2) & 3);
-      pending = ik;
+      pending = bk;
       __builtin_amdgcn_sched_barrier(0);  // regions A and B are scheduled separately
-      // region A
-      qk(std::integral_constant<int, (sl + 1) & 3>{}, snext);
-      weights(scur, pf);
-      // keep the K operand reads 3 ahead of the MFMAs that use them
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS read
+      // region A: the K operand reads run 3 ahead of their MFMAs, and each MFMA has
+      // one pair of tile j's weights next to it (fences keep that order)
+      {
+        constexpr int sl1 = (sl + 1) & 3;
+        const unsigned char* kb = smem + KBUF + sl1 * KT_BYTES;
+        constexpr int NPAIR = 8;  // weight pairs per lane and tile
+        static_assert(NPAIR % KS == 0 || KS % NPAIR == 0, "pairs must spread evenly over the k-steps");
+        float l0 = 0.f, l1 = 0.f;
+        u32x4 kf[KS];
 #pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);  // VALU incl. exp
-        if (i + 3 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        for (int ks = 0; ks < 3 && ks < KS; ++ks) kf[ks] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ (ks << 5)));
+        snext = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 3 < KS) kf[ks + 3] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ ((ks + 3) << 5)));
+          snext = mfma32(kf[ks], qf[ks], snext);
+#pragma unroll
+          for (int pp = ks * NPAIR / KS; pp < (ks + 1) * NPAIR / KS; ++pp) {
+            const int v = pp >> 2, w = pp & 3;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[8 * v + 2 * w], c2, -m));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[8 * v + 2 * w + 1], c2, -m));
+            const uint32_t pk = pack2(p0, p1);
+            pf[v][w] = pk;
+            if (w & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l1, false);
+            else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l0, false);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        ls = l0 + l1;
       }
+      check(scur, pf, ls);
       __builtin_amdgcn_sched_barrier(0);
       // region B
       pv(std::integral_constant<int, sl>{}, std::false_type{}, j, pf);
-      const float mx = row_max(snext);
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);  // LDS read
 #pragma unroll
       for (int i = 0; i < 2 * DB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x402, 1, 1);  // VALU
         if (i + 3 < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
       }
-      settle(j + 1, snext, mx);
+      __builtin_amdgcn_sched_barrier(0);
+      mask(j + 1, snext);
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(kIssuePerStep) : "memory");
     };
-    // The last tile: weights and P V with the sequence-end clip, nothing to issue.
+    // The last tile: weights, check and P V with the sequence-end clip; nothing to issue.
     auto last = [&](auto slot_tag, f32x16& scur) {
-      weights(scur, pf);
+      weights(scur, pf, ls);
+      check(scur, pf, ls);
       pv(slot_tag, std::true_type{}, t1 - 1, pf);
     };
     int u = 0;

@@ -21,8 +21,11 @@ from synth import Workload
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 # Tolerances on the output: bf16 inputs with fp32 accumulation, and fp32.
+# lse (natural log) for bf16: the row sum adds the softmax weights after their
+# rounding to bf16 (relative error <= 2^-9 each, nearest even), so the sum is off by
+# a factor within 1 +- 2^-9 and lse by at most 2^-9 ~ 1.95e-3, plus fp32 terms ~1e-6.
 TOL = {
-    "bf16": {"max": 2e-2, "mean": 2e-3, "lse": 1e-3},
+    "bf16": {"max": 2e-2, "mean": 2e-3, "lse": 2e-3},
     "f32": {"max": 1e-5, "mean": 1e-5, "lse": 1e-5},
 }
 
