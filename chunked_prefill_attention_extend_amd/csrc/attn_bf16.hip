@@ -345,7 +345,8 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
         if (key_of_elem(i, 0) > t) s[i] = -INFINITY;
     }
   };
-  // Weights p = 2^(s c - m) as packed bf16 for the P.V product, and this lane's sum
+  // Scores are kept shifted, s c - m (log2 units), from the region after their QK
+  // product on. Weights p = 2^s as packed bf16 for the P.V product, and this lane's sum
   // of them over the tile. The sum adds the same bf16 values (a dot product with
   // ones), so the normalisation matches the numerator of P.V exactly.
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -355,8 +356,8 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     for (int v = 0; v < 2; ++v)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * v + 2 * w], c2, -m));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * v + 2 * w + 1], c2, -m));
+        const float p0 = __builtin_amdgcn_exp2f(s[8 * v + 2 * w]);
+        const float p1 = __builtin_amdgcn_exp2f(s[8 * v + 2 * w + 1]);
         // (the packed value goes through a local: a bit cast of a vector element
         // lvalue such as pf[v][w] has been seen to read element 0)
         const uint32_t pk = pack2(p0, p1);
@@ -367,21 +368,28 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     ls = l0 + l1;
   };
   // Check of a tile's weights before they enter P.V: when some lane's sum passed
-  // kSumBound (or overflowed), raise m to the rows' exact max over the tile, rescale
-  // O and l, and redo the weights. Then add the tile's sum to l.
-  auto check = [&](const f32x16& s, u32x4 (&pf)[2], float& ls) {
+  // kSumBound (or overflowed), raise m by the rows' exact max over the (shifted)
+  // tile, rescale O and l, shift the tile again and redo its weights. The next
+  // tile's scores are shifted afterwards, with the new m. Then add the sum to l.
+  auto check = [&](f32x16& s, u32x4 (&pf)[2], float& ls) {
     if (__builtin_amdgcn_ballot_w64(ls > kSumBound) != 0) {
-      float mx = row_max(s) * c2;
+      float mx = row_max(s);
       mx = fmaxf(mx, partner(mx, hi));
-      const float d = fmaxf(mx - m, 0.f);
+      const float d = fmaxf(mx, 0.f);
       const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       l *= alpha;
       m += d;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] -= d;
       weights(s, pf, ls);
     }
     l += ls;
+  };
+  auto shift = [&](f32x16& s) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = fmaf(s[i], c2, -m);
   };
   // O^T += V^T P^T for one tile from V ring slot `slot` (compile-time). With `clip`
   // (only the last tile of the range), values past the sequence end read as zero:
@@ -432,12 +440,13 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       mx = fmaxf(mx, partner(mx, hi));
       m = (mx == -INFINITY) ? 0.f : mx;
     }
+    shift(sa);
     // Steady step u (tile j = t0 + u, not the last): S(j) is in scur (masked), K(j+1)
     // in K slot (u+1)%4, V(j) in V slot u%4. Issue K(j+3) and V(j+2) (their slots
     // were last read two steps ago); then
     //   region A: S(j+1) = QK(j+1) MFMAs interleaved with tile j's weights,
     //   check tile j's weights (rare path: raise m),
-    //   region B: O += P(j) V(j) MFMAs,
+    //   region B: O += P(j) V(j) MFMAs interleaved with the shift of S(j+1),
     // then mask tile j+1 if it is a diagonal tile.
     auto step = [&](auto slot_tag, int u, f32x16& scur, f32x16& snext) {
       constexpr int sl = decltype(slot_tag)::value;  // u % 4
@@ -470,8 +479,8 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
 #pragma unroll
           for (int pp = ks * NPAIR / KS; pp < (ks + 1) * NPAIR / KS; ++pp) {
             const int v = pp >> 2, w = pp & 3;
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(scur[8 * v + 2 * w], c2, -m));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(scur[8 * v + 2 * w + 1], c2, -m));
+            const float p0 = __builtin_amdgcn_exp2f(scur[8 * v + 2 * w]);
+            const float p1 = __builtin_amdgcn_exp2f(scur[8 * v + 2 * w + 1]);
             const uint32_t pk = pack2(p0, p1);
             pf[v][w] = pk;
             if (w & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l1, false);
@@ -483,12 +492,14 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       }
       check(scur, pf, ls);
       __builtin_amdgcn_sched_barrier(0);
-      // region B
+      // region B (with the shift of tile j+1's scores)
       pv(std::integral_constant<int, sl>{}, std::false_type{}, j, pf);
+      shift(snext);
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);  // LDS read
 #pragma unroll
       for (int i = 0; i < 2 * DB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 16 / (2 * DB), 1);  // VALU
         if (i + 3 < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
       }
       __builtin_amdgcn_sched_barrier(0);
