@@ -58,13 +58,14 @@ __device__ inline int key_of_elem(int i, int hi) { return ((i >> 3) << 4) + (hi 
 
 __device__ inline u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
-// Zero the bf16 values of a 16-byte V piece whose keys k0 .. k0+7 reach kv_len.
+// Zero the bf16 values of a 16-byte V piece whose keys k0 .. k0+7 reach kv_len
+// (branch-free: a per-lane branch here would split the wave's control flow).
 __device__ inline u32x4 clip_keys(u32x4 v, int k0, int kv_len) {
-  if (k0 + 8 <= kv_len) return v;
+  const int n = kv_len - k0;  // keys of the piece that are inside
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const uint32_t lo = (k0 + 2 * w < kv_len) ? 0x0000ffffu : 0u;
-    const uint32_t hi = (k0 + 2 * w + 1 < kv_len) ? 0xffff0000u : 0u;
+    const uint32_t lo = (2 * w < n) ? 0x0000ffffu : 0u;
+    const uint32_t hi = (2 * w + 1 < n) ? 0xffff0000u : 0u;
     v[w] &= (lo | hi);
   }
   return v;
@@ -590,52 +591,61 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
 
   // Keys (within the 32-key tile) this lane loads as MFMA rows of blocks 0 / 1.
   const int kbase = 8 * (l16 >> 2) + (l16 & 3);
+  // This wave's tiles [tw0, tw1) of the item's key range.
+  const int nt = (it.key_end - it.key_begin + kSplitTile - 1) / kSplitTile;
+  const int tw0 = wave * nt / kWaves, tw1 = (wave + 1) * nt / kWaves;
+  // All block ids of the wave's range in one load (one per lane), checked once:
+  // ids outside [0, num_blocks) become -1 (read the zero page) and are counted;
+  // entries past the sequence end are -1 too. No tile load then waits on an id.
+  static_assert(kSplitKeysMax / kSplitTile / kWaves * (kSplitTile / kBlockSize) <= 64, "ids of a wave fit one per lane");
+  int32_t idw = -1;
+  {
+    const int lb = (it.key_begin + tw0 * kSplitTile) / kBlockSize + lane;
+    const bool inside = lane < (tw1 - tw0) * (kSplitTile / kBlockSize) && lb < nblk;
+    const int32_t v = inside ? bt[lb] : -1;
+    const bool ok = block_ok(v, a.num_blocks);
+    const uint64_t bad = __builtin_amdgcn_ballot_w64(inside && !ok);
+    if (bad != 0 && lane == 0) atomicAdd(a.err, int(__builtin_popcountll(bad)));
+    idw = (inside && ok) ? v : -1;
+  }
+  const unsigned char* zp = static_cast<const unsigned char*>(a.zero_page);
+  auto blk_base = [&](const uint16_t* cache, int32_t blk) -> const uint16_t* {
+    return blk < 0 ? reinterpret_cast<const uint16_t*>(zp) : cache + (int64_t(blk) * a.hkv + g) * (kBlockSize * D);
+  };
   struct Tile {
     u32x4 kf[2][KS];
     u32x4 vf[DB];
     int kt;
-    bool ok0, ok1;
   };
-  // Loads are unconditional (invalid block ids read block 0); validity and the
-  // sequence end are applied when the tile is consumed, so the next tile's
-  // loads stay in flight while this one is computed.
+  // Loads are unconditional (invalid blocks and blocks past the end read the zero
+  // page); the sequence end is applied when the tile is consumed, so the next
+  // tile's loads stay in flight while this one is computed.
   auto load = [&](int jj, Tile& T) {
     const int kt = it.key_begin + jj * kSplitTile;
-    const int lb0 = kt / kBlockSize;
-    const int32_t p0 = lb0 < nblk ? bt[lb0] : -1;
-    const int32_t p1 = lb0 + 1 < nblk ? bt[lb0 + 1] : -1;
-    const bool ok0 = block_ok(p0, a.num_blocks), ok1 = block_ok(p1, a.num_blocks);
-    if (lane == 0) {
-      if (lb0 < nblk && !ok0) atomicAdd(a.err, 1);
-      if (lb0 + 1 < nblk && !ok1) atomicAdd(a.err, 1);
-    }
-    const int32_t s0 = ok0 ? p0 : 0, s1 = ok1 ? p1 : 0;
+    const int e = 2 * (jj - tw0);
+    const int32_t s0 = __builtin_amdgcn_readlane(idw, e), s1 = __builtin_amdgcn_readlane(idw, e + 1);
+    const uint16_t* kb0 = blk_base(kc, s0);
+    const uint16_t* kb1 = blk_base(kc, s1);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int koff = kbase + 4 * b;  // < 32; block koff / 16
-      const int32_t pk = koff < kBlockSize ? s0 : s1;
-      const uint16_t* kp = kc + ((int64_t(pk) * a.hkv + g) * kBlockSize + (koff % kBlockSize)) * D + q4 * 8;
+      const uint16_t* kp = (koff < kBlockSize ? kb0 : kb1) + (koff % kBlockSize) * D + q4 * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) T.kf[b][ks] = *reinterpret_cast<const u32x4*>(kp + ks * 32);
     }
-    const int32_t pv = q4 < 2 ? s0 : s1;
-    const uint16_t* vp = vc + (int64_t(pv) * a.hkv + g) * (kBlockSize * D) + 8 * (q4 & 1);
+    const uint16_t* vp = (q4 < 2 ? blk_base(vc, s0) : blk_base(vc, s1)) + 8 * (q4 & 1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) T.vf[db] = *reinterpret_cast<const u32x4*>(vp + (db * 16 + l16) * kBlockSize);
     T.kt = kt;
-    T.ok0 = ok0;
-    T.ok1 = ok1;
   };
   auto compute = [&](Tile& T) {
     const int kt = T.kt;
     f32x4 sc[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int koff = kbase + 4 * b;
-      const bool okk = (koff < kBlockSize ? T.ok0 : T.ok1) && kt + koff < kv_len;
       sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sc[b] = mfma16(okk ? T.kf[b][ks] : zero4(), qf[ks], sc[b]);
+      for (int ks = 0; ks < KS; ++ks) sc[b] = mfma16(T.kf[b][ks], qf[ks], sc[b]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (kt + 8 * q4 + 4 * b + i > lim) sc[b][i] = -INFINITY;
@@ -667,25 +677,20 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       pf[2 * b] = pack2(p0, p1);
       pf[2 * b + 1] = pack2(p2, p3);
     }
-    const bool okv = q4 < 2 ? T.ok0 : T.ok1;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const u32x4 vv = okv ? clip_keys(T.vf[db], kt + 8 * q4, kv_len) : zero4();
-      o[db] = mfma16(vv, pf, o[db]);
-    }
+    for (int db = 0; db < DB; ++db) o[db] = mfma16(clip_keys(T.vf[db], kt + 8 * q4, kv_len), pf, o[db]);
   };
 
-  const int nt = (it.key_end - it.key_begin + kSplitTile - 1) / kSplitTile;
-  const int tw0 = wave * nt / kWaves, tw1 = (wave + 1) * nt / kWaves;
+  // Two tiles in flight. Loads are issued whether or not the tile is used (tiles
+  // past the wave's range read the zero page): a load under a branch would make the
+  // compiler wait for it where the branches join.
   Tile ta, tb;
-  if (tw0 < tw1) load(tw0, ta);
+  load(tw0, ta);
   for (int jj = tw0; jj < tw1; jj += 2) {
-    if (jj + 1 < tw1) load(jj + 1, tb);
+    load(jj + 1, tb);
     compute(ta);
-    if (jj + 1 < tw1) {
-      if (jj + 2 < tw1) load(jj + 2, ta);
-      compute(tb);
-    }
+    load(jj + 2, ta);
+    if (jj + 1 < tw1) compute(tb);
   }
 
   // Merge the waves' partial results through LDS (the page's merge rule over the

@@ -16,7 +16,9 @@ constexpr int kRowsPerWave = 32;  // query rows per wave (one 32x32 MFMA column 
 constexpr int kRowsPerTile = kWaves * 32;  // chunk path: all waves' rows share each K/V tile
 constexpr int kChunkKeys = 32;    // chunk path: keys per LDS K/V tile (one 32x32 S^T block)
 constexpr int kSplitTile = 32;    // split path: keys per register K/V tile
-constexpr int kSplitKeys = 2048;  // split path: keys per workgroup (kWaves waves)
+constexpr int kSplitKeysMin = 1024;  // split path: keys per workgroup (kWaves waves), lower bound
+constexpr int kSplitKeysMax = 8192;  // upper bound: a wave's block ids fit one per lane
+constexpr int kSplitTargetItems = 512;  // split path aims at this many workgroups (2 per CU on 256 CUs)
 constexpr int kSplitRows = 16;    // split path: at most this many rows (one 16-row MFMA block)
 
 // Per-request metadata copied to the workspace.
@@ -111,6 +113,7 @@ struct Plan {
   std::vector<WorkItem> items;
   std::vector<CombineTask> tasks;
   int64_t n_slots = 0;
+  int32_t split_keys = 0;  // keys per split workgroup (0: no split items)
   int64_t total_rows = 0;
   // byte offsets inside the workspace
   size_t off_zero = 0, off_seqs = 0, off_items = 0, off_tasks = 0, off_slots = 0, bytes = 0, upload_bytes = 0;

@@ -42,7 +42,7 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Work list of one launch. Requests whose E * group rows fit one 16-row MFMA
 // block (decode rows, short verify rows) take the split path: the key range is cut into
-// kSplitKeys pieces (one workgroup each, one part per wave); each workgroup
+// pieces (one workgroup each, one part per wave); each workgroup
 // merges its waves' parts and leaves one partial result, and the combine kernel
 // merges the workgroups' partials. Longer chunks take the chunk path:
 // kRowsPerTile-row tiles over their whole causal key range.
@@ -53,6 +53,7 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
   plan.items.clear();
   plan.tasks.clear();
   plan.n_slots = 0;
+  plan.split_keys = 0;
   int64_t q_off = 0;
   for (int32_t r = 0; r < num_seqs; ++r) {
     plan.seqs[r] = SeqInfo{static_cast<int32_t>(q_off), prefix[r], extend[r], 0};
@@ -62,17 +63,29 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
 
   if (dtype == EXTATTN_BF16) {
     std::vector<WorkItem> chunk_items, split_items;
+    // Keys per split workgroup: every workgroup pays a fixed start-up (ids, first
+    // loads in flight) while it holds its CU alone, so pieces are as long as the
+    // work allows while still giving about kSplitTargetItems workgroups; a multiple
+    // of kWaves tiles, between kSplitKeysMin and kSplitKeysMax.
+    int64_t split_keys = 0;
+    for (int32_t r = 0; r < num_seqs; ++r)
+      if (int64_t(extend[r]) * group <= kSplitRows) split_keys += (int64_t(prefix[r]) + extend[r]) * hkv;
+    constexpr int64_t kGrain = int64_t(kSplitTile) * kWaves;
+    int64_t piece = (split_keys + kSplitTargetItems - 1) / kSplitTargetItems;
+    piece = (piece + kGrain - 1) / kGrain * kGrain;
+    piece = std::min<int64_t>(std::max<int64_t>(piece, kSplitKeysMin), kSplitKeysMax);
+    plan.split_keys = int32_t(piece);
     for (int32_t r = 0; r < num_seqs; ++r) {
       const int64_t rows = int64_t(extend[r]) * group;
       const int64_t kv_len = int64_t(prefix[r]) + extend[r];
       if (rows <= kSplitRows) {
-        const int64_t nwg = (kv_len + kSplitKeys - 1) / kSplitKeys;
+        const int64_t nwg = (kv_len + piece - 1) / piece;
         for (int32_t g = 0; g < hkv; ++g) {
           const int64_t slot0 = nwg > 1 ? plan.n_slots : -1;
           const int32_t task = nwg > 1 ? int32_t(plan.tasks.size()) : -1;
           for (int64_t w = 0; w < nwg; ++w) {
-            const int64_t kb = w * kSplitKeys;
-            const int64_t ke = std::min<int64_t>(kv_len, kb + kSplitKeys);
+            const int64_t kb = w * piece;
+            const int64_t ke = std::min<int64_t>(kv_len, kb + piece);
             split_items.push_back(WorkItem{kItemSplit, r, g, 0, int32_t(rows), int32_t(kb), int32_t(ke),
                                            int32_t(nwg > 1 ? slot0 + w : -1), task, {0, 0, 0}});
           }
