@@ -136,21 +136,27 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
     flush = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev)
 
     def timed(fn):
-        ts = []
+        """GPU time of one call (its metadata copy and kernels), median over reps. The
+        GPU is first given a few ms of fills so that the host enqueues every call ahead
+        of the GPU: the events then bracket device work only, not host-side planning."""
+        torch.cuda.synchronize()
+        for _ in range(20):
+            flush.fill_(0x5A)
+        evs = []
         for i in range(reps + 2):
             flush.fill_(i & 0xFF)   # evict the 256 MB last-level cache between repetitions
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             fn()
             b.record()
-            torch.cuda.synchronize()
-            if i >= 2:
-                ts.append(a.elapsed_time(b) * 1e-3)
-        return float(np.median(ts))
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) * 1e-3 for a, b in evs[2:]]
+        return float(np.median(ts)), float(np.min(ts))
 
-    t_mix = timed(lambda: ext.extend_attention(q, k_cache, v_cache, bt, prefix, extend, w.scale, out, lse,
+    (t_mix, t_mix_min) = timed(lambda: ext.extend_attention(q, k_cache, v_cache, bt, prefix, extend, w.scale, out, lse,
                                                workspace=ws))
-    t_dec = timed(lambda: ext.extend_attention(q_dec, k_cache, v_cache, bt_dec, [prefix[i] for i in dec],
+    (t_dec, t_dec_min) = timed(lambda: ext.extend_attention(q_dec, k_cache, v_cache, bt_dec, [prefix[i] for i in dec],
                                                [1] * len(dec), w.scale, out_dec, lse_dec, workspace=ws))
     dec_bytes = 0
     for i in dec:
@@ -161,14 +167,52 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
     return {
         "workload": "mixed_budget2048: 64 decode rows (context U{512..8192}) + 1984-row chunk at P=6144, "
                     "32 q / 8 kv heads, D=128, bf16, one launch",
+        "timing": "GPU time per call (metadata copy + kernels), median of %d calls, host enqueued ahead" % reps,
         "ms_mixed_launch": t_mix * 1e3,
+        "ms_mixed_launch_min": t_mix_min * 1e3,
         "ms_decode_rows_only": t_dec * 1e3,
+        "ms_decode_rows_only_min": t_dec_min * 1e3,
         "decode_bytes": dec_bytes,
         "decode_GBps": dec_bytes / t_dec / 1e9,
         "decode_frac_hbm_peak": dec_bytes / t_dec / 1e9 / PEAK_HBM_GBS,
         "chunk_flops": chunk_flops,
         "mixed_lower_bound_ms": max(chunk_flops / (PEAK_BF16_TFLOPS * 1e12), dec_bytes / (PEAK_HBM_GBS * 1e9)) * 1e3,
     }
+
+
+def calibration(torch):
+    """Reference rates on this GPU, for reading the rooflines: a vendor bf16 GEMM on
+    random data (the practical matrix-core rate, which sits below the published dense
+    peak when operands are random) and a plain device copy (HBM)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    n = 8192
+    a = (torch.randn((n, n), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    b = (torch.randn((n, n), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    nb = 1 << 30
+    src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2.0 * nb * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return {"gemm_bf16_8192_random_tflops": gemm, "copy_1gib_read_plus_write_gbps": copy}
 
 
 def cpu_baseline(target_s: float = 15.0):
@@ -261,6 +305,12 @@ def main() -> int:
     kern_s = sum(a.elapsed_time(b) for step in events for a, b in step) * 1e-3 / args.steps
     per_launch_s = kern_s / nchunk
     achieved = flops / nchunk / per_launch_s / 1e12
+    # per chunk: median over the timed steps
+    med = [float(np.median([events[k][t][0].elapsed_time(events[k][t][1]) * 1e-3 for k in range(args.steps)]))
+           for t in range(nchunk)]
+    chunk_f = [sweep_flops([pe], SWEEP["hq"], SWEEP["d"]) for pe in s["plan"]]
+    per_chunk = {f"t{t}": chunk_f[t] / med[t] / 1e12 for t in (0, 1, 3, 7, 15, 31, 63, 95, 127) if t < nchunk}
+    aggregate = sum(chunk_f) / sum(med) / 1e12
     ms = dt / args.steps * 1e3
     value = flops / (dt / args.steps) / 1e12
 
@@ -268,6 +318,8 @@ def main() -> int:
     if not args.no_mixed:
         log("mixed step")
         mixed = mixed_step_bench(torch, ext, synth)
+    log("calibration")
+    calib = calibration(torch)
     base = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
@@ -293,6 +345,9 @@ def main() -> int:
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                      "kernel": "attn_bf16_kernel<128>",
                      "avg_launch_ms": per_launch_s * 1e3, "flops_per_launch": flops / nchunk},
+        "sweep_attention": {"aggregate_tflops": aggregate, "per_chunk_tflops": per_chunk,
+                            "note": "attention launches only (kv_append excluded); sum(F) / sum(per-chunk median)"},
+        "calibration": calib,
         "mixed_step": mixed,
         "cpu_baseline": base,
     }
