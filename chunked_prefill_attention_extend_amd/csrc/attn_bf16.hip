@@ -283,8 +283,12 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     if (bad != 0 && wave == 0 && lane == 0) atomicAdd(a.err, int(__builtin_popcountll(bad)));
     idwin = (inside && ok) ? v : -1;
   };
-  // This wave's block id of tile j (wave-uniform).
-  auto read_blk = [&](int j) -> int32_t { return __builtin_amdgcn_readlane(idwin, ((j - t0) & 31) * 2 + my_blk); };
+  // This wave's block id of tile j (wave-uniform); tiles past the range (padding
+  // steps) read the zero page even where the sequence still has keys.
+  auto read_blk = [&](int j) -> int32_t {
+    const int32_t v = __builtin_amdgcn_readlane(idwin, ((j - t0) & 31) * 2 + my_blk);
+    return j < t1 ? v : -1;
+  };
   auto block_base = [&](const uint16_t* cache, int32_t blk) -> const unsigned char* {
     return blk < 0 ? static_cast<const unsigned char*>(a.zero_page)
                    : reinterpret_cast<const unsigned char*>(cache + (int64_t(blk) * a.hkv + g) * (kBlockSize * D));
@@ -392,22 +396,34 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = fmaf(s[i], c2, -m);
   };
-  // O^T += V^T P^T for one tile from V ring slot `slot` (compile-time). With `clip`
-  // (only the last tile of the range), values past the sequence end read as zero:
-  // their weights are zero but the cache slots may hold anything.
-  auto pv = [&](auto slot_tag, auto clip_tag, int j, const u32x4 (&pf)[2]) {
+  // O^T += V^T P^T for one tile from V ring slot `slot` (compile-time).
+  auto pv = [&](auto slot_tag, const u32x4 (&pf)[2]) {
     constexpr int slot = decltype(slot_tag)::value;
-    constexpr bool clip = decltype(clip_tag)::value;
     const unsigned char* base = smem + VBUF + slot * KT_BYTES;
-    const int kt = j * KT;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int b = 0; b < 2; ++b) {  // 16-key block of the tile; this lane's keys 16 b + 8 hi .. +8
-        u32x4 vf = *reinterpret_cast<const u32x4*>(base + v_off + b * VSUB + db * 32 * (kBlockSize * 2));
-        if (clip) vf = clip_keys(vf, kt + 16 * b + 8 * hi, kv_len);
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(base + v_off + b * VSUB + db * 32 * (kBlockSize * 2));
         o[db] = mfma32(vf, pf[b], o[db]);
       }
+  };
+  // Values of keys past the sequence end read as zero: their weights are zero but the
+  // cache slots may hold anything (0 * NaN would poison O). Only the range's last tile
+  // can reach past the end; its V tile is cleared in LDS once, after it has landed
+  // and before it is read (the caller puts barriers around this).
+  const bool tail_clip = (t1 * KT > kv_len);
+  auto clip_tail = [&](int slot) {
+    unsigned char* base = smem + VBUF + slot * KT_BYTES;
+    const int kt = (t1 - 1) * KT;
+    for (int piece = tid; piece < 4 * D; piece += kThreads) {  // 16-byte pieces of the V tile
+      const int b = piece / (2 * D), d = (piece / 2) % D, h = piece & 1;
+      const int key0 = kt + 16 * b + 8 * (h ^ swz_v(d));
+      if (key0 + 8 > kv_len) {
+        u32x4* pp = reinterpret_cast<u32x4*>(base + b * VSUB + d * (kBlockSize * 2) + h * 16);
+        *pp = clip_keys(*pp, key0, kv_len);
+      }
+    }
   };
 
   if (n > 0) {
@@ -430,6 +446,10 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     int32_t pending = read_blk(t0 + 2);  // tile j+2: K issued, V not yet
     issue_k(pending, 2);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (tail_clip && n == 1) {  // the first tile is the last one
+      clip_tail(0);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
     f32x16 sa, sb;
     u32x4 pf[2];
     float ls;
@@ -494,7 +514,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       check(scur, pf, ls);
       __builtin_amdgcn_sched_barrier(0);
       // region B (with the shift of tile j+1's scores)
-      pv(std::integral_constant<int, sl>{}, std::false_type{}, j, pf);
+      pv(std::integral_constant<int, sl>{}, pf);
       shift(snext);
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);  // LDS read
 #pragma unroll
@@ -506,37 +526,28 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       __builtin_amdgcn_sched_barrier(0);
       mask(j + 1, snext);
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(kIssuePerStep) : "memory");
+      if (tail_clip && j + 1 == t1 - 1) {  // V(j+1) has landed: clear its keys past the end
+        clip_tail((sl + 1) & 3);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
     };
     // The last tile: weights, check and P V with the sequence-end clip; nothing to issue.
-    auto last = [&](auto slot_tag, f32x16& scur) {
+    auto last = [&](f32x16& scur) {
       weights(scur, pf, ls);
       check(scur, pf, ls);
-      pv(slot_tag, std::true_type{}, t1 - 1, pf);
+      pv(std::integral_constant<int, 0>{}, pf);
     };
-    int u = 0;
-    for (; u + 4 < n; u += 4) {
+    // The step count is rounded up so that the 4-way unrolled loop needs no remainder:
+    // tiles past the range's end read the zero page and are masked out entirely.
+    const int npad = n + ((1 - n) & 3);  // npad = 1 (mod 4), npad >= n
+    for (int u = 0; u + 4 < npad; u += 4) {
       step(std::integral_constant<int, 0>{}, u, sa, sb);
       step(std::integral_constant<int, 1>{}, u + 1, sb, sa);
       step(std::integral_constant<int, 2>{}, u + 2, sa, sb);
       step(std::integral_constant<int, 3>{}, u + 3, sb, sa);
     }
-    // 1 to 4 tiles remain (u = n-4 .. n-1); S(t0+u) is in sa
-    const int rem = n - u;
-    if (rem == 1) {
-      last(std::integral_constant<int, 0>{}, sa);
-    } else if (rem == 2) {
-      step(std::integral_constant<int, 0>{}, u, sa, sb);
-      last(std::integral_constant<int, 1>{}, sb);
-    } else if (rem == 3) {
-      step(std::integral_constant<int, 0>{}, u, sa, sb);
-      step(std::integral_constant<int, 1>{}, u + 1, sb, sa);
-      last(std::integral_constant<int, 2>{}, sa);
-    } else {
-      step(std::integral_constant<int, 0>{}, u, sa, sb);
-      step(std::integral_constant<int, 1>{}, u + 1, sb, sa);
-      step(std::integral_constant<int, 2>{}, u + 2, sa, sb);
-      last(std::integral_constant<int, 3>{}, sb);
-    }
+    // tile t0 + npad - 1 (npad - 1 is a multiple of 4): S in sa, V in ring slot 0
+    last(sa);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads issued past the end
   }
   write_row<D>(a, o, m, l, valid, hi, orow, it.slot < 0 ? -1 : it.slot + wave, rloc);
