@@ -47,19 +47,29 @@ def log(msg: str) -> None:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_sweep128k_traffic.json")
 
 
+def code_hash(files) -> str:
+    """sha256 over the given sources with // comments and blank lines removed, so
+    that only code changes (not comment edits) count as a changed kernel."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in files:
+        for line in open(os.path.join(ROOT, f), encoding="utf-8"):
+            code = re.sub(r"//.*", "", line).rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs (copy-calibrated), or None when the kernel sources changed
+    WRITE_SIZE runs (copy-calibrated), or None when the kernel code changed
     since those counters were taken."""
-    import hashlib
     try:
         t = json.load(open(TRAFFIC_FILE))
-        h = hashlib.sha256()
-        for f in t["source_files"]:
-            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if code_hash(t["source_files"]) != t.get("code_sha256"):
+            return None
     except (OSError, ValueError, KeyError):
-        return None
-    if h.hexdigest() != t.get("source_sha256"):
         return None
     return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
 

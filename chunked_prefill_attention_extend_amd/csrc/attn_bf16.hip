@@ -9,15 +9,17 @@
 // Split key ranges end in a partial (o, lse) that the combine kernel merges
 // with the same rule.
 //
-// Layout of the work (one workgroup = 4 wave64):
+// Layout of the work (one workgroup = 8 wave64, 2 per SIMD, one per CU):
 //  * Rows are (position, head-in-group) pairs of one (request, KV head): the
 //    whole GQA group shares each K/V tile.
-//  * Chunk items: 128 rows, the 4 waves hold 32 rows each; K/V tiles of 64
-//    keys are copied from the paged cache into LDS once per workgroup
-//    (double buffered, one barrier per tile) and read by all 4 waves.
+//  * Chunk items: 256 rows, 32 per wave; 32-key K/V tiles are copied from the
+//    paged cache straight into 4-slot LDS rings once per workgroup and read by
+//    all 8 waves (one barrier per tile).
 //  * Split items (<= 16 rows: decode rows, short verify rows): every wave
 //    reads its own part of the key range straight from HBM into MFMA operand
-//    registers (no LDS) and leaves a partial result for the combine kernel.
+//    registers (no LDS); the waves' parts are merged in LDS, and a workgroup
+//    whose range is part of a longer context leaves a partial result for the
+//    combine kernel.
 //
 // The contraction runs transposed: S^T = K Q^T and O^T = V^T P^T on
 // v_mfma_f32_32x32x16_bf16. A lane then owns one query row (column l % 32 of
@@ -144,22 +146,22 @@ __device__ inline void write_row(const AttnArgs& a, const f32x16 (&o)[D / 32], f
 }
 
 // ---------------------------------------------------------------------------
-// Chunk items: 128 rows, LDS-shared K/V tiles of 64 keys.
+// Chunk items: 256 rows, LDS-shared K/V tiles of 32 keys.
 //
 // K/V tiles go from the paged cache straight into LDS (global_load_lds_dwordx4:
 // each lane's 16 bytes land at the instruction's LDS base + 16 * lane), so no
-// registers hold the next tile. Each wave issues 1/4 of a tile per buffer.
-// LDS layouts (per stage):
-//   K: 64 rows (keys) x D bf16; 16-byte piece p of row r sits at position
+// registers hold the next tile. Each wave copies one 1 KB piece of every K and
+// every V tile. LDS layouts (per ring slot):
+//   K: 32 rows (keys) x D bf16; 16-byte piece p of row r sits at position
 //      p ^ swz_k(r), swz_k(r) = key_of_row(r % 16) (mod pieces per row).
-//   V: four sub-tiles, one per 16-key block, each D rows (features) x 16 keys;
+//   V: two sub-tiles, one per 16-key block, each D rows (features) x 16 keys;
 //      half h (8 keys) of row d sits at position h ^ swz_v(d),
 //      swz_v(d) = ((d >> 2) ^ (d >> 3)) & 1.
-// Wave w loads block w of the tile for both K and V, so every direct load has
-// one block (a uniform base address) and a 32-bit per-lane offset.
-// Both keep every aligned group of 8 (and of 16) lanes of a 16-byte LDS read on
-// distinct banks. Tiles that reach past the sequence end or hold an invalid
-// block id are masked when read; all others are read as they are.
+// A piece lies inside one cache block, so every direct load has a uniform base
+// address and a 32-bit per-lane offset. Both swizzles keep every aligned group
+// of 8 (and of 16) lanes of a 16-byte LDS read on distinct banks. Invalid block
+// ids and tiles past the range read a page of zeros; keys past the range are
+// masked in the scores, and values past the sequence end are cleared in LDS.
 // ---------------------------------------------------------------------------
 __device__ inline int swz_v(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
 
