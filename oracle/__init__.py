@@ -14,6 +14,7 @@ function here is "parity unpinned".
 """
 
 from .chunk_plan import chunk_plan, effective_length  # noqa: F401
+from .budget import decode_first_with_slack, mixed_chunk_step, slack_limit, token_budget_step  # noqa: F401
 from .attention import (  # noqa: F401
     attend_rows,
     causal_attention,
