@@ -10,8 +10,11 @@ from .binding import (  # noqa: F401
     EXTATTN_F32,
     LIB_PATH,
     chunk_plan,
+    decode_first_with_slack,
     extend_attention,
     kv_append,
     load_library,
+    mixed_chunk_step,
+    token_budget_step,
     workspace_bytes,
 )

@@ -41,6 +41,19 @@ def load_library() -> ctypes.CDLL:
     lib.extattn_chunk_plan.restype = ctypes.c_int
     lib.extattn_chunk_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_double, _c_i64p, _c_i64p,
                                        _c_i64p, _c_i64p, _c_i64p, ctypes.c_int64]
+    _c_i32p_ = ctypes.POINTER(ctypes.c_int32)
+    lib.extattn_token_budget_step.restype = ctypes.c_int
+    lib.extattn_token_budget_step.argtypes = [ctypes.c_int32, _c_i64p, _c_i64p, ctypes.c_int32, _c_i64p, _c_i64p,
+                                              ctypes.c_int64, _c_i32p_, _c_i64p, _c_i64p, ctypes.c_int32,
+                                              _c_i32p_, _c_i64p]
+    lib.extattn_mixed_chunk_step.restype = ctypes.c_int
+    lib.extattn_mixed_chunk_step.argtypes = [ctypes.c_int32, _c_i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                             _c_i64p, _c_i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                             _c_i32p_, _c_i32p_, _c_i64p, _c_i64p, ctypes.c_int32, _c_i32p_,
+                                             _c_i64p, _c_i32p_, _c_i32p_, _c_i64p]
+    lib.extattn_decode_first_with_slack.restype = ctypes.c_int
+    lib.extattn_decode_first_with_slack.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                    _c_i64p, _c_i64p, _c_i64p]
     lib.extattn_workspace_bytes.restype = ctypes.c_int
     lib.extattn_workspace_bytes.argtypes = [ctypes.c_int32, _c_i32p, _c_i32p, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
@@ -105,6 +118,84 @@ def chunk_plan(n_tokens: int, chunk_size: int, hit_rate: float = 0.0) -> dict:
                                   e.ctypes.data_as(_c_i64p), n))
     return {"cached": cached.value, "effective": eff.value,
             "chunks": [(int(p[t]), int(e[t])) for t in range(n)]}
+
+
+def _i64(values) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(list(values), dtype=np.int64))
+    return a if a.size else np.zeros(1, np.int64)
+
+
+def token_budget_step(running, waiting, budget: int):
+    """One mixed step under a token budget (see ``extattn_token_budget_step``).
+
+    running: [(total_tokens, computed)], waiting: [(total_tokens, cached)].
+    Returns ``(entries, budget_left)`` with entries ``(kind, index, prefix, extend)``,
+    kind ``"running"`` or ``"waiting"``, in scheduling order."""
+    lib = load_library()
+    running, waiting = list(running), list(waiting)
+    rt, rc_ = _i64(t for t, _ in running), _i64(c for _, c in running)
+    wt, wc = _i64(t for t, _ in waiting), _i64(c for _, c in waiting)
+    cap = len(running) + len(waiting)
+    idx = np.zeros(max(cap, 1), np.int32)
+    pre = np.zeros(max(cap, 1), np.int64)
+    ext = np.zeros(max(cap, 1), np.int64)
+    n, left = ctypes.c_int32(), ctypes.c_int64()
+    _check(lib.extattn_token_budget_step(len(running), rt.ctypes.data_as(_c_i64p), rc_.ctypes.data_as(_c_i64p),
+                                         len(waiting), wt.ctypes.data_as(_c_i64p), wc.ctypes.data_as(_c_i64p),
+                                         int(budget), idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                         pre.ctypes.data_as(_c_i64p), ext.ctypes.data_as(_c_i64p), cap,
+                                         ctypes.byref(n), ctypes.byref(left)))
+    out = []
+    for k in range(n.value):
+        i = int(idx[k])
+        kind, j = ("running", i) if i < len(running) else ("waiting", i - len(running))
+        out.append((kind, j, int(pre[k]), int(ext[k])))
+    return out, left.value
+
+
+_KINDS = {0: "decode", 1: "chunked", 2: "waiting"}
+
+
+def mixed_chunk_step(decode_prefix, chunked, waiting, chunk_size: int, page_size: int = 1, mixed: bool = True):
+    """One round of the mixed-chunk scheduler (see ``extattn_mixed_chunk_step``).
+
+    decode_prefix: cached tokens of each decode row; chunked: None or (total, done);
+    waiting: [(total_tokens, cached)]. Returns ``(entries, chunk_left, next_chunked)``:
+    entries ``(kind, index, prefix, extend)``, kind "decode" | "chunked" | "waiting";
+    next_chunked None or ``(kind, index, total, done)``."""
+    lib = load_library()
+    decode_prefix, waiting = list(decode_prefix), list(waiting)
+    dp = _i64(decode_prefix)
+    wt, wc = _i64(t for t, _ in waiting), _i64(c for _, c in waiting)
+    ct, cd = (int(chunked[0]), int(chunked[1])) if chunked is not None else (0, 0)
+    cap = len(decode_prefix) + 1 + len(waiting)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    kinds, idx = np.zeros(cap, np.int32), np.zeros(cap, np.int32)
+    pre, ext = np.zeros(cap, np.int64), np.zeros(cap, np.int64)
+    n, left, nk, ni, nd = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(lib.extattn_mixed_chunk_step(len(decode_prefix), dp.ctypes.data_as(_c_i64p), ct, cd, len(waiting),
+                                        wt.ctypes.data_as(_c_i64p), wc.ctypes.data_as(_c_i64p), int(chunk_size),
+                                        int(page_size), 1 if mixed else 0, kinds.ctypes.data_as(i32p),
+                                        idx.ctypes.data_as(i32p), pre.ctypes.data_as(_c_i64p),
+                                        ext.ctypes.data_as(_c_i64p), cap, ctypes.byref(n), ctypes.byref(left),
+                                        ctypes.byref(nk), ctypes.byref(ni), ctypes.byref(nd)))
+    entries = [(_KINDS[int(kinds[k])], int(idx[k]), int(pre[k]), int(ext[k])) for k in range(n.value)]
+    nxt = None
+    if nk.value >= 0:
+        total = ct if nk.value == 1 else int(waiting[ni.value][0])
+        nxt = (_KINDS[nk.value], ni.value, total, nd.value)
+    return entries, left.value, nxt
+
+
+def decode_first_with_slack(ready_decode: int, pending_prefill: int, chunk_query_len: int,
+                            max_batched_tokens: int):
+    """``(p_step, d_step, limit)`` of the default mixed-step scheduler."""
+    lib = load_library()
+    p, d, lim = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.extattn_decode_first_with_slack(int(ready_decode), int(pending_prefill), int(chunk_query_len),
+                                               int(max_batched_tokens), ctypes.byref(p), ctypes.byref(d),
+                                               ctypes.byref(lim)))
+    return p.value, d.value, lim.value
 
 
 def _dtype_code(t) -> int:

@@ -133,6 +133,45 @@ extern "C" {
 
 const char* extattn_last_error(void) { return g_error.c_str(); }
 
+int extattn_token_budget_step(int32_t n_running, const int64_t* running_total, const int64_t* running_computed,
+                              int32_t n_waiting, const int64_t* waiting_total, const int64_t* waiting_cached,
+                              int64_t budget, int32_t* out_index, int64_t* out_prefix, int64_t* out_extend,
+                              int32_t capacity, int32_t* n_out, int64_t* budget_left) {
+  const char* why = "";
+  const int rc = extattn::token_budget_step_impl(n_running, running_total, running_computed, n_waiting, waiting_total,
+                                                 waiting_cached, budget, out_index, out_prefix, out_extend, capacity,
+                                                 n_out, budget_left, &why);
+  if (rc != EXTATTN_OK) return fail(rc, why);
+  g_error.clear();
+  return EXTATTN_OK;
+}
+
+int extattn_mixed_chunk_step(int32_t n_decode, const int64_t* decode_prefix, int64_t chunked_total,
+                             int64_t chunked_done, int32_t n_waiting, const int64_t* waiting_total,
+                             const int64_t* waiting_cached, int64_t chunk_size, int64_t page_size, int32_t mixed,
+                             int32_t* out_kind, int32_t* out_index, int64_t* out_prefix, int64_t* out_extend,
+                             int32_t capacity, int32_t* n_out, int64_t* chunk_left, int32_t* next_kind,
+                             int32_t* next_index, int64_t* next_done) {
+  const char* why = "";
+  const int rc = extattn::mixed_chunk_step_impl(n_decode, decode_prefix, chunked_total, chunked_done, n_waiting,
+                                                waiting_total, waiting_cached, chunk_size, page_size, mixed, out_kind,
+                                                out_index, out_prefix, out_extend, capacity, n_out, chunk_left,
+                                                next_kind, next_index, next_done, &why);
+  if (rc != EXTATTN_OK) return fail(rc, why);
+  g_error.clear();
+  return EXTATTN_OK;
+}
+
+int extattn_decode_first_with_slack(int64_t ready_decode, int64_t pending_prefill, int64_t chunk_query_len,
+                                    int64_t max_batched_tokens, int64_t* p_step, int64_t* d_step, int64_t* limit) {
+  const char* why = "";
+  const int rc = extattn::decode_first_with_slack_impl(ready_decode, pending_prefill, chunk_query_len,
+                                                       max_batched_tokens, p_step, d_step, limit, &why);
+  if (rc != EXTATTN_OK) return fail(rc, why);
+  g_error.clear();
+  return EXTATTN_OK;
+}
+
 int extattn_chunk_plan(int64_t n_tokens, int64_t chunk_size, double hit_rate, int64_t* cached,
                        int64_t* effective, int64_t* n_chunks, int64_t* prefix_lens, int64_t* extend_lens,
                        int64_t capacity) {

@@ -126,6 +126,21 @@ constexpr size_t kZeroPageBytes = size_t(kBlockSize) * 128 * 4;  // one (block, 
 int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
                int32_t head_dim, int32_t dtype, Plan& plan);
 
+// budget.cpp
+int token_budget_step_impl(int32_t n_running, const int64_t* running_total, const int64_t* running_computed,
+                           int32_t n_waiting, const int64_t* waiting_total, const int64_t* waiting_cached,
+                           int64_t budget, int32_t* out_index, int64_t* out_prefix, int64_t* out_extend,
+                           int32_t capacity, int32_t* n_out, int64_t* budget_left, const char** why);
+int mixed_chunk_step_impl(int32_t n_decode, const int64_t* decode_prefix, int64_t chunked_total,
+                          int64_t chunked_done, int32_t n_waiting, const int64_t* waiting_total,
+                          const int64_t* waiting_cached, int64_t chunk_size, int64_t page_size, int32_t mixed,
+                          int32_t* out_kind, int32_t* out_index, int64_t* out_prefix, int64_t* out_extend,
+                          int32_t capacity, int32_t* n_out, int64_t* chunk_left, int32_t* next_kind,
+                          int32_t* next_index, int64_t* next_done, const char** why);
+int decode_first_with_slack_impl(int64_t ready_decode, int64_t pending_prefill, int64_t chunk_query_len,
+                                 int64_t max_batched_tokens, int64_t* p_step, int64_t* d_step, int64_t* limit,
+                                 const char** why);
+
 // kernel launchers (one per .hip file)
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_combine(const AttnArgs& a, int32_t dtype, hipStream_t stream);

@@ -61,6 +61,77 @@ enum {
 
 enum { EXTATTN_BF16 = 0, EXTATTN_F32 = 1 };
 
+/* Entry kinds of extattn_mixed_chunk_step. */
+enum { EXTATTN_ENTRY_DECODE = 0, EXTATTN_ENTRY_CHUNKED = 1, EXTATTN_ENTRY_WAITING = 2 };
+
+/*
+ * One mixed step under a token budget (host only, pure, thread-safe).
+ *
+ * Source: token-budget blog ("2.4 Chunked Prefill and the unified token
+ * budget"), section 4 (a step is one map {request: tokens} whose sum is bounded
+ * by the budget) and section 5 (the budget cuts chunks): running requests are
+ * served first, in order, each with min(tokens still needed, budget left); then
+ * waiting requests in queue order the same way, starting after their prefix-cache
+ * hits, until the budget is used up. KV-cache allocation and preemption are not
+ * modelled (every allocation succeeds).
+ *
+ * Running request i still needs running_total[i] - running_computed[i] >= 1
+ * tokens (1 for a decode row); waiting request i needs waiting_total[i] -
+ * waiting_cached[i] >= 1. Outputs (host arrays of `capacity` entries, scheduling
+ * order): out_index (i for running i, n_running + i for waiting i), out_prefix
+ * (tokens already in the cache: the launch's prefix_lens), out_extend (tokens this
+ * step: the launch's extend_lens); *n_out entries and *budget_left are written on
+ * EXTATTN_OK and EXTATTN_ENOSPC.
+ * Errors: EXTATTN_EINVAL for budget < 1, negative queue sizes, null arrays, a
+ * request with nothing left to compute; EXTATTN_ENOSPC if capacity < *n_out.
+ */
+int extattn_token_budget_step(int32_t n_running, const int64_t* running_total, const int64_t* running_computed,
+                              int32_t n_waiting, const int64_t* waiting_total, const int64_t* waiting_cached,
+                              int64_t budget, int32_t* out_index, int64_t* out_prefix, int64_t* out_extend,
+                              int32_t capacity, int32_t* n_out, int64_t* budget_left);
+
+/*
+ * One round of the mixed-chunk scheduler (host only, pure, thread-safe).
+ *
+ * Source: zdszero notes, sections "only one half-finished request", "four things
+ * per round", "mixed chunk" and "page alignment only at the first cut". With
+ * `mixed` set, every decode row takes one token (prefix decode_prefix[i],
+ * extend 1) and the running batch is taken out of the chunk budget first, so a
+ * slice is chunk_size - n_decode. The half-finished request (chunked_total > 0,
+ * chunked_done tokens done) continues first, without page alignment; waiting
+ * requests then fill what is left in queue order, and the first one that does not
+ * fit is cut with its end aligned down to a multiple of page_size and becomes the
+ * next half-finished request (if alignment leaves nothing it waits).
+ *
+ * Outputs (host arrays of `capacity` entries): out_kind (EXTATTN_ENTRY_*),
+ * out_index (decode row, 0 for the half-finished request, waiting index),
+ * out_prefix, out_extend; *n_out, *chunk_left (budget not used) and the next
+ * half-finished request (*next_kind = -1 if none, else its kind, *next_index and
+ * *next_done = tokens done after this round) are written on EXTATTN_OK and
+ * EXTATTN_ENOSPC.
+ * Errors: EXTATTN_EINVAL for chunk_size or page_size < 1, negative sizes, null
+ * arrays, 0 <= chunked_done < chunked_total violated, a waiting request with
+ * nothing left; EXTATTN_ENOSPC if capacity < *n_out.
+ */
+int extattn_mixed_chunk_step(int32_t n_decode, const int64_t* decode_prefix, int64_t chunked_total,
+                             int64_t chunked_done, int32_t n_waiting, const int64_t* waiting_total,
+                             const int64_t* waiting_cached, int64_t chunk_size, int64_t page_size, int32_t mixed,
+                             int32_t* out_kind, int32_t* out_index, int64_t* out_prefix, int64_t* out_extend,
+                             int32_t capacity, int32_t* n_out, int64_t* chunk_left, int32_t* next_kind,
+                             int32_t* next_index, int64_t* next_done);
+
+/*
+ * Default mixed-step scheduler of the msmodeling chunked-prefill RFC, section
+ * 3.1.4 (host only, pure): d_step = min(ready_decode, max_batched_tokens),
+ * limit = floor(max_batched_tokens * 1.15) as one IEEE double multiply (so a
+ * budget of 100 gives 114), p_step = max(0, min(pending_prefill,
+ * floor((limit - d_step) / chunk_query_len))).
+ * Errors: EXTATTN_EINVAL for negative counts, chunk_query_len < 1,
+ * max_batched_tokens < 1 or null outputs.
+ */
+int extattn_decode_first_with_slack(int64_t ready_decode, int64_t pending_prefill, int64_t chunk_query_len,
+                                    int64_t max_batched_tokens, int64_t* p_step, int64_t* d_step, int64_t* limit);
+
 /*
  * Chunk plan of one prompt (host only, pure, thread-safe).
  *

@@ -151,3 +151,19 @@ def test_device_argument_errors():
     small = torch.empty(256, dtype=torch.uint8, device="cuda")
     with pytest.raises(ValueError):
         ext.extend_attention(q, cache.k, cache.v, cache.bt, [16], [16], 0.1, out, workspace=small)
+
+
+def test_planner_to_launch_budget2048():
+    """A queue planned by the library's token-budget step (the token-budget blog's
+    section-5 example: budget 2048, 8 decode rows, a running prefill needing 1440,
+    a waiting 900-token prompt cut to 600) run as one launch and checked against
+    the oracle."""
+    running = [(1001 + 37 * i, 1000 + 37 * i) for i in range(8)] + [(3000, 1560)]
+    waiting = [(900, 0), (500, 0)]
+    entries, left = ext.token_budget_step(running, waiting, 2048)
+    assert [e[3] for e in entries] == [1] * 8 + [1440, 600] and left == 0
+    launches = [(e[2], e[3]) for e in entries]
+    w = custom_workload(2048, launches, 32, 8, 128)
+    log(f"planned launch {launches}")
+    out, lse, q_off, q = run_launch(w)
+    check_launch(w, out, lse, q_off, q, what="planned budget-2048 step")
