@@ -225,6 +225,52 @@ def calibration(torch):
     return {"gemm_bf16_8192_random_tflops": gemm, "copy_1gib_read_plus_write_gbps": copy}
 
 
+def chunk_size_sweep(torch, ext, synth, n: int = 65536, sizes=(256, 512, 1024, 2048, 4096, 8192, 16384),
+                     reps: int = 3):
+    """Attention TFLOP/s of one prompt of n tokens prefilled at each chunk size C
+    (64 q / 8 kv heads, D=128, bf16, sweep-style inputs): the zdszero notes' claim
+    that one forward's efficiency saturates past some size, measured for this
+    kernel. The cache is filled once (the tokens are the same for every C);
+    each chunk's attention launch is timed with HIP events, median of reps."""
+    hq, hkv, d = SWEEP["hq"], SWEEP["hkv"], SWEEP["d"]
+    bf = torch.bfloat16
+    nb = n // 16
+    q = synth.device_normal((n, hq, d), 5101, 0.5, bf)
+    k_new = synth.device_normal((n, hkv, d), 5102, 0.5, bf)
+    v_new = synth.device_normal((n, hkv, d), 5103, 0.5, bf)
+    k_cache = torch.zeros((nb, hkv, 16, d), dtype=bf, device="cuda")
+    v_cache = torch.zeros((nb, hkv, d, 16), dtype=bf, device="cuda")
+    perm = np.random.default_rng(5104).permutation(nb).astype(np.int32)
+    bt = torch.from_numpy(perm.reshape(1, nb)).cuda()
+    ext.kv_append(k_new, v_new, k_cache, v_cache, bt, [0], [n])
+    out = torch.empty_like(q)
+    lse = torch.empty((n, hq), dtype=torch.float32, device="cuda")
+    rows = []
+    for c in sizes:
+        plan = ext.chunk_plan(n, c, 0.0)["chunks"]
+        ws = torch.empty(max(ext.workspace_bytes([p], [e], hq, hkv, d, ext.EXTATTN_BF16) for p, e in plan),
+                         dtype=torch.uint8, device="cuda")
+        times = []
+        for _ in range(reps + 1):
+            evs = []
+            for p, e in plan:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                ext.extend_attention(q[p:p + e], k_cache, v_cache, bt, [p], [e], 1.0 / math.sqrt(d),
+                                     out[p:p + e], lse[p:p + e], workspace=ws)
+                b.record()
+                evs.append((a, b))
+            torch.cuda.synchronize()
+            times.append(sum(a.elapsed_time(b) for a, b in evs) * 1e-3)
+        t = float(np.median(times[1:]))
+        f = sweep_flops(plan, hq, d)
+        rows.append({"chunk_size": c, "chunks": len(plan), "attention_ms": t * 1e3, "tflops": f / t / 1e12,
+                     "ms_per_chunk": t * 1e3 / len(plan)})
+        log(f"chunk size {c}: {len(plan)} chunks, {t * 1e3:.2f} ms, {f / t / 1e12:.0f} TFLOP/s")
+    return {"workload": f"one prompt of {n} tokens, 64 q / 8 kv heads, D=128, bf16, paged block 16, permuted blocks",
+            "flops": sweep_flops(ext.chunk_plan(n, sizes[0], 0.0)["chunks"], hq, d), "rows": rows}
+
+
 def cpu_baseline(target_s: float = 15.0):
     """Time the CPU oracle on sampled rows of the sweep (chunk 64, P = 65536)."""
     import oracle
@@ -266,6 +312,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--only-mixed", action="store_true", help="run only the mixed-step measurement (for profiling)")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="only measure attention TFLOP/s against the chunk size (one 64k prompt)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 launches), the reference for HBM byte counters")
     args = ap.parse_args()
@@ -290,6 +338,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n, "bytes_written_per_launch": n,
                                                "launches": 3}}), flush=True)
+        return 0
+    if args.chunk_sweep:
+        print(json.dumps({"chunk_size_sweep": chunk_size_sweep(torch, ext, synth)}), flush=True)
         return 0
     if args.only_mixed:
         print(json.dumps({"mixed_step": mixed_step_bench(torch, ext, synth)}), flush=True)

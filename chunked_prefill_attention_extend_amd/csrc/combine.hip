@@ -23,22 +23,22 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   const CombineTask t = a.tasks[blockIdx.x];
   const SeqInfo s = a.seqs[t.seq];
   const int sub = threadIdx.x % kTpr;
-  const size_t sf = slot_floats(D);
   for (int r = threadIdx.x / kTpr; r < t.nrows; r += kRpp) {
+    const int sr = t.srow0 + r;  // row within the slots
     float mx = -INFINITY;
     for (int i = 0; i < t.nslots; ++i) {
-      const float* sl = a.slots + size_t(t.slot0 + i * t.stride) * sf;
-      mx = fmaxf(mx, sl[kRowsPerWave * D + r]);
+      const float* sl = a.slots + int64_t(t.slot0) + int64_t(i) * t.stride;
+      mx = fmaxf(mx, sl[t.slot_rows * D + sr]);
     }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     for (int i = 0; i < t.nslots; ++i) {
-      const float* sl = a.slots + size_t(t.slot0 + i * t.stride) * sf;
-      const float L = sl[kRowsPerWave * D + r];
+      const float* sl = a.slots + int64_t(t.slot0) + int64_t(i) * t.stride;
+      const float L = sl[t.slot_rows * D + sr];
       if (L == -INFINITY) continue;
       const float w = expf(L - mx);
       wsum += w;
-      const float4 o = *reinterpret_cast<const float4*>(sl + r * D + sub * 4);
+      const float4 o = *reinterpret_cast<const float4*>(sl + sr * D + sub * 4);
       acc[0] = fmaf(w, o.x, acc[0]);
       acc[1] = fmaf(w, o.y, acc[1]);
       acc[2] = fmaf(w, o.z, acc[2]);

@@ -19,6 +19,9 @@ constexpr int kSplitTile = 32;    // split path: keys per register K/V tile
 constexpr int kSplitKeysMin = 1024;  // split path: keys per workgroup (kWaves waves), lower bound
 constexpr int kSplitKeysMax = 8192;  // upper bound: a wave's block ids fit one per lane
 constexpr int kSplitTargetItems = 512;  // split path aims at this many workgroups (2 per CU on 256 CUs)
+constexpr int kChunkTargetItems = 256;  // chunk rows: split key ranges until about this many workgroups (1 per CU)
+constexpr int kChunkMinPieceKeys = 2048;  // ... with at least this many keys per piece
+constexpr int kCombineRows = 32;         // rows per combine task of split chunk tiles
 constexpr int kSplitRows = 16;    // split path: at most this many rows (one 16-row MFMA block)
 
 // Per-request metadata copied to the workspace.
@@ -42,27 +45,31 @@ struct WorkItem {
   int32_t kv_head;
   int32_t row0;       // first flattened row
   int32_t nrows;      // rows in this item (<= kRowsPerTile chunk, <= kSplitRows split)
-  int32_t key_begin;  // keys [key_begin, key_end); key_begin is a multiple of 64
+  int32_t key_begin;  // keys [key_begin, key_end); key_begin is a multiple of kChunkKeys
   int32_t key_end;
-  int32_t slot;       // < 0: write out/lse directly; else the partial slot (chunk: one per wave, split: one)
-  int32_t task;       // split items: combine task that merges this workgroup's slot, or -1 (direct write)
+  int32_t slot;       // < 0: write out/lse directly; else float offset of this item's partial slot
+  int32_t task;       // combine task that merges this item's slot, or -1 (direct write)
   int32_t pad[3];
 };
 
-// Merge of partial results for <= 32 rows of one (request, KV head).
+// Merge of the partial results of rows [row0, row0 + nrows) of one (request, KV
+// head): rows srow0 .. srow0 + nrows - 1 of the slots at float offsets
+// slot0 + i * stride, i in [0, nslots), each slot holding slot_rows rows.
 struct CombineTask {
   int32_t seq;
   int32_t kv_head;
   int32_t row0;
   int32_t nrows;
-  int32_t slot0;   // slots slot0 + i * stride, i in [0, nslots)
+  int32_t slot0;
   int32_t nslots;
   int32_t stride;
-  int32_t pad;
+  int32_t slot_rows;
+  int32_t srow0;
+  int32_t pad[3];
 };
 
-// Partial slot: o (normalised, fp32) [32][D] then lse (natural log) [32].
-inline constexpr size_t slot_floats(int head_dim) { return size_t(kRowsPerWave) * head_dim + kRowsPerWave; }
+// A partial slot of `rows` rows: o (normalised, fp32) [rows][D] then lse (natural log) [rows].
+inline constexpr size_t slot_floats(int rows, int head_dim) { return size_t(rows) * (head_dim + 1); }
 
 struct AttnArgs {
   const void* q;
@@ -112,7 +119,7 @@ struct Plan {
   std::vector<SeqInfo> seqs;
   std::vector<WorkItem> items;
   std::vector<CombineTask> tasks;
-  int64_t n_slots = 0;
+  int64_t n_slot_floats = 0;  // size of the partial-slot area
   int32_t split_keys = 0;  // keys per split workgroup (0: no split items)
   int64_t total_rows = 0;
   // byte offsets inside the workspace

@@ -52,7 +52,7 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
   plan.seqs.resize(num_seqs);
   plan.items.clear();
   plan.tasks.clear();
-  plan.n_slots = 0;
+  plan.n_slot_floats = 0;
   plan.split_keys = 0;
   int64_t q_off = 0;
   for (int32_t r = 0; r < num_seqs; ++r) {
@@ -75,35 +75,68 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
     piece = (piece + kGrain - 1) / kGrain * kGrain;
     piece = std::min<int64_t>(std::max<int64_t>(piece, kSplitKeysMin), kSplitKeysMax);
     plan.split_keys = int32_t(piece);
+    // Chunk rows: when the chunk tiles alone cannot fill the GPU (short chunks, few
+    // heads), each tile's key range is cut into pieces, one workgroup each, and the
+    // combine kernel merges the pieces by the page's rule (the one-GPU share of a
+    // context-parallel split of the prefix).
+    int64_t chunk_tiles = 0;
+    for (int32_t r = 0; r < num_seqs; ++r) {
+      const int64_t rows = int64_t(extend[r]) * group;
+      if (rows > kSplitRows) chunk_tiles += (rows + kRowsPerTile - 1) / kRowsPerTile * hkv;
+    }
+    const int64_t chunk_pieces =
+        chunk_tiles > 0 ? std::max<int64_t>(1, (kChunkTargetItems + chunk_tiles - 1) / chunk_tiles) : 1;
     for (int32_t r = 0; r < num_seqs; ++r) {
       const int64_t rows = int64_t(extend[r]) * group;
       const int64_t kv_len = int64_t(prefix[r]) + extend[r];
       if (rows <= kSplitRows) {
         const int64_t nwg = (kv_len + piece - 1) / piece;
+        const int64_t sf = int64_t(slot_floats(kSplitRows, head_dim));
         for (int32_t g = 0; g < hkv; ++g) {
-          const int64_t slot0 = nwg > 1 ? plan.n_slots : -1;
+          const int64_t slot0 = plan.n_slot_floats;
           const int32_t task = nwg > 1 ? int32_t(plan.tasks.size()) : -1;
           for (int64_t w = 0; w < nwg; ++w) {
             const int64_t kb = w * piece;
             const int64_t ke = std::min<int64_t>(kv_len, kb + piece);
             split_items.push_back(WorkItem{kItemSplit, r, g, 0, int32_t(rows), int32_t(kb), int32_t(ke),
-                                           int32_t(nwg > 1 ? slot0 + w : -1), task, {0, 0, 0}});
+                                           int32_t(nwg > 1 ? slot0 + w * sf : -1), task, {0, 0, 0}});
           }
           if (nwg > 1) {
-            plan.tasks.push_back(CombineTask{r, g, 0, int32_t(rows), int32_t(slot0), int32_t(nwg), 1, 0});
-            plan.n_slots += nwg;
+            plan.tasks.push_back(CombineTask{r, g, 0, int32_t(rows), int32_t(slot0), int32_t(nwg), int32_t(sf),
+                                             kSplitRows, 0, {0, 0, 0}});
+            plan.n_slot_floats += nwg * sf;
           }
         }
       } else {
         const int64_t ntiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
+        const int64_t sf = int64_t(slot_floats(kRowsPerTile, head_dim));
         for (int32_t g = 0; g < hkv; ++g) {
           for (int64_t t = 0; t < ntiles; ++t) {
             const int64_t row0 = t * kRowsPerTile;
             const int64_t nrows = std::min<int64_t>(kRowsPerTile, rows - row0);
             const int64_t pos_max = (row0 + nrows - 1) / group;
             const int64_t key_end = int64_t(prefix[r]) + pos_max + 1;
-            chunk_items.push_back(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), 0,
-                                           int32_t(key_end), -1, -1, {0, 0, 0}});
+            const int64_t ktiles = (key_end + kChunkKeys - 1) / kChunkKeys;
+            const int64_t pieces = std::max<int64_t>(1, std::min<int64_t>(chunk_pieces, key_end / kChunkMinPieceKeys));
+            if (pieces == 1) {
+              chunk_items.push_back(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), 0,
+                                             int32_t(key_end), -1, -1, {0, 0, 0}});
+              continue;
+            }
+            // pieces of about equal tile counts; the last one holds the diagonal
+            const int64_t slot0 = plan.n_slot_floats;
+            const int32_t task0 = int32_t(plan.tasks.size());
+            for (int64_t i = 0; i < pieces; ++i) {
+              const int64_t kb = ktiles * i / pieces * kChunkKeys;
+              const int64_t ke = i + 1 < pieces ? ktiles * (i + 1) / pieces * kChunkKeys : key_end;
+              chunk_items.push_back(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), int32_t(kb),
+                                             int32_t(ke), int32_t(slot0 + i * sf), task0, {0, 0, 0}});
+            }
+            for (int64_t sr = 0; sr < nrows; sr += kCombineRows)
+              plan.tasks.push_back(CombineTask{r, g, int32_t(row0 + sr),
+                                               int32_t(std::min<int64_t>(kCombineRows, nrows - sr)), int32_t(slot0),
+                                               int32_t(pieces), int32_t(sf), kRowsPerTile, int32_t(sr), {0, 0, 0}});
+            plan.n_slot_floats += pieces * sf;
           }
         }
       }
@@ -130,7 +163,7 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
   off = align_up(off + sizeof(CombineTask) * plan.tasks.size(), 256);
   plan.upload_bytes = off;
   plan.off_slots = off;
-  off = align_up(off + sizeof(float) * slot_floats(head_dim) * size_t(plan.n_slots), 256);
+  off = align_up(off + sizeof(float) * size_t(plan.n_slot_floats), 256);
   plan.bytes = off;
   return EXTATTN_OK;
 }

@@ -60,6 +60,8 @@ def test_sweep128k_sampled_chunks():
     ([(77, 5)], 64, 8, 128),              # 40 rows: one partial chunk tile
     ([(300, 17)], 64, 1, 128),            # one KV head for 64 query heads
     ([(4095, 1), (16, 1), (1, 1)], 32, 8, 64),  # decode rows, D=64
+    ([(6000, 700)], 32, 8, 128),          # 88 chunk tiles: key ranges cut in 3 pieces and merged; ragged end
+    ([(5000, 256)], 16, 2, 64),           # 16 chunk tiles, D=64: 2 pieces
 ])
 def test_edge_cases(case):
     launches, hq, hkv, d = case
