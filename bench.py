@@ -190,6 +190,61 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
     }
 
 
+def verify_rows_sweep(torch, ext, synth, reps: int = 10):
+    """Multi-token verify rows (several candidate tokens per request, as in
+    speculative decoding): the 64 requests of the mixed step (context L ~
+    U{512..8192}, 32 or 64 q / 8 kv heads, D=128, bf16), each launched with its last E
+    tokens as query rows (P = L - E) for E = 1..8. Like decode rows these are
+    HBM-bound (up to G*E = 64 rows per KV head share one read of the context), so the
+    figure is bytes / GPU time against the 8 TB/s peak."""
+    w = synth.make_workload("mixed_budget2048")
+    dev = "cuda"
+    bf = torch.bfloat16
+    reqs = [r for r in w.requests if r.launch[1] == 1]
+    hkv, d = w.n_kv_heads, w.head_dim
+    k_cache = torch.zeros((w.num_blocks, hkv, 16, d), dtype=bf, device=dev)
+    v_cache = torch.zeros((w.num_blocks, hkv, d, 16), dtype=bf, device=dev)
+    bt_all = w.block_table()
+    ctx = [r.n_ctx for r in reqs]
+    for r in reqs:
+        kk = synth.device_normal((r.n_ctx, hkv, d), 6000 + r.index, 0.5, bf)
+        vv = synth.device_normal((r.n_ctx, hkv, d), 7000 + r.index, 0.5, bf)
+        ext.kv_append(kk, vv, k_cache, v_cache, torch.from_numpy(bt_all[r.index:r.index + 1]).to(dev), [0],
+                      [r.n_ctx])
+    bt = torch.from_numpy(bt_all[:len(reqs)]).to(dev)
+    flush = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev)
+    rows = []
+    for hq, e in [(h, x) for h in (32, 64) for x in range(1, 9)]:
+        prefix = [L - e for L in ctx]
+        extend = [e] * len(ctx)
+        q = synth.device_normal((e * len(ctx), hq, d), 6900 + e, 0.5, bf)
+        out = torch.empty_like(q)
+        lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=dev)
+        ws = torch.empty(ext.workspace_bytes(prefix, extend, hq, hkv, d, ext.EXTATTN_BF16), dtype=torch.uint8,
+                         device=dev)
+        torch.cuda.synchronize()
+        for _ in range(20):
+            flush.fill_(0x5A)
+        evs = []
+        for i in range(reps + 2):
+            flush.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            ext.extend_attention(q, k_cache, v_cache, bt, prefix, extend, w.scale, out, lse, workspace=ws)
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        t = float(np.median([a.elapsed_time(b) * 1e-3 for a, b in evs[2:]]))
+        nbytes = sum(2 * L * hkv * d * 2 + 2 * e * hq * d * 2 + 4 * e * hq + 4 * math.ceil(L / 16) for L in ctx)
+        rows.append({"q_heads": hq, "E": e, "rows_per_kv_head": e * hq // hkv, "ms": t * 1e3, "bytes": nbytes,
+                     "GBps": nbytes / t / 1e9, "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBS})
+        log(f"verify Hq={hq} E={e}: {t * 1e3:.3f} ms, {nbytes / t / 1e9:.0f} GB/s")
+    return {"workload": "64 requests, context U{512..8192} (the mixed step's decode contexts), last E tokens as "
+                        "query rows, 32 or 64 q / 8 kv heads, D=128, bf16, one launch per (Hq, E)",
+            "timing": "GPU time per call (metadata copy + kernels), median of %d calls, LLC flushed" % reps,
+            "rows": rows}
+
+
 def calibration(torch):
     """Reference rates on this GPU, for reading the rooflines: a vendor bf16 GEMM on
     random data (the practical matrix-core rate, which sits below the published dense
@@ -316,6 +371,8 @@ def main() -> int:
                     help="only measure attention TFLOP/s against the chunk size (one 64k prompt)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 launches), the reference for HBM byte counters")
+    ap.add_argument("--verify-sweep", action="store_true",
+                    help="only measure verify rows (E = 1..8 query rows per request) in HBM GB/s")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -341,6 +398,9 @@ def main() -> int:
         return 0
     if args.chunk_sweep:
         print(json.dumps({"chunk_size_sweep": chunk_size_sweep(torch, ext, synth)}), flush=True)
+        return 0
+    if args.verify_sweep:
+        print(json.dumps({"verify_rows": verify_rows_sweep(torch, ext, synth)}), flush=True)
         return 0
     if args.only_mixed:
         print(json.dumps({"mixed_step": mixed_step_bench(torch, ext, synth)}), flush=True)

@@ -15,9 +15,10 @@
 //  * Chunk items: 256 rows, 32 per wave; 32-key K/V tiles are copied from the
 //    paged cache straight into 4-slot LDS rings once per workgroup and read by
 //    all 8 waves (one barrier per tile).
-//  * Split items (<= 16 rows: decode rows, short verify rows): every wave
-//    reads its own part of the key range straight from HBM into MFMA operand
-//    registers (no LDS); the waves' parts are merged in LDS, and a workgroup
+//  * Split items (<= 32 rows: decode rows, multi-token verify rows): every
+//    wave takes all the rows and reads its own part of the key range straight
+//    from HBM into MFMA operand registers (no LDS); the waves' parts are merged
+//    in LDS, and a workgroup
 //    whose range is part of a longer context leaves a partial result for the
 //    combine kernel.
 //
@@ -556,13 +557,17 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
 }
 
 // ---------------------------------------------------------------------------
-// Split items: <= 16 rows (decode rows, short verify rows); each wave streams
-// its own part of the key range from HBM straight into MFMA operand registers,
-// two 32-key tiles in flight. These run on v_mfma_f32_16x16x32_bf16 (16 query
-// rows per wave). Accumulator element i of lane l belongs to query row l % 16
-// and MFMA row 4 (l / 16) + i; MFMA row r of key block b holds key
-// 8 (r / 4) + 4 b + r % 4 of the tile, so each lane's P^T operand (4 values
-// from block 0, 4 from block 1) covers 8 consecutive keys.
+// Split items: <= 32 rows (decode rows, multi-token verify rows); each wave
+// streams its own part of the key range from HBM straight into MFMA operand
+// registers. These run on v_mfma_f32_16x16x32_bf16 with RB = 1 or 2 blocks of 16
+// query rows per wave; the RB blocks share every K/V operand, so the context is
+// read once whatever the row count. Accumulator element i of lane l belongs to
+// query row l % 16 of its block and MFMA row 4 (l / 16) + i; MFMA row r of key
+// block b holds key 8 (r / 4) + 4 b + r % 4 of the tile, so each lane's P^T
+// operand (4 values from block 0, 4 from block 1) covers 8 consecutive keys.
+// With one row block two 32-key tiles are in flight per wave; with two, the
+// second block's operands take the registers of the second tile, and the next
+// tile is loaded as soon as the current one has been consumed.
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -571,36 +576,46 @@ __device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  c, 0, 0, 0);
 }
 
-template <int D>
+template <int D, int RB>
 __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char* smem) {
   constexpr int KS = D / 32;  // 32-wide k-steps over the head dim
   constexpr int DB = D / 16;  // 16-feature blocks of O^T
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
+  const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const SeqInfo si = a.seqs[it.seq];
   const int G = a.group, g = it.kv_head;
   const int kv_len = si.prefix + si.extend;
-  const bool valid = l16 < it.nrows;
-  const int pos = valid ? l16 / G : 0;
-  const int hh = valid ? l16 - pos * G : 0;
-  const int64_t orow = int64_t(si.q_off + pos) * a.hq + g * G + hh;
-  const int lim = valid ? min(si.prefix + pos, it.key_end - 1) : -1;
 
-  u32x4 qf[KS];
-  {
+  // Row block rb of this lane: row rb * 16 + l16 of the item.
+  u32x4 qf[RB][KS];
+  int lim[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rr = rb * kSplitRows + l16;
+    const bool valid = rr < it.nrows;
+    const int pos = valid ? rr / G : 0;
+    const int hh = valid ? rr - pos * G : 0;
+    const int64_t orow = int64_t(si.q_off + pos) * a.hq + g * G + hh;
+    lim[rb] = valid ? min(si.prefix + pos, it.key_end - 1) : -1;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + orow * D + q4 * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = valid ? *reinterpret_cast<const u32x4*>(qp + ks * 32) : zero4();
+    for (int ks = 0; ks < KS; ++ks) qf[rb][ks] = valid ? *reinterpret_cast<const u32x4*>(qp + ks * 32) : zero4();
   }
   const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
   const int nblk = (kv_len + kBlockSize - 1) / kBlockSize;
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
 
-  f32x4 o[DB];
+  f32x4 o[RB][DB];
+  float m[RB], l[RB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+  }
 
   // Keys (within the 32-key tile) this lane loads as MFMA rows of blocks 0 / 1.
   const int kbase = 8 * (l16 >> 2) + (l16 & 3);
@@ -635,7 +650,8 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   // tile's loads stay in flight while this one is computed.
   auto load = [&](int jj, Tile& T) {
     const int kt = it.key_begin + jj * kSplitTile;
-    const int e = 2 * (jj - tw0);
+    // tiles loaded past the wave's range may index past lane 63: any valid id will do
+    const int e = (2 * (jj - tw0)) & 63;
     const int32_t s0 = __builtin_amdgcn_readlane(idw, e), s1 = __builtin_amdgcn_readlane(idw, e + 1);
     const uint16_t* kb0 = blk_base(kc, s0);
     const uint16_t* kb1 = blk_base(kc, s1);
@@ -653,92 +669,115 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   };
   auto compute = [&](Tile& T) {
     const int kt = T.kt;
-    f32x4 sc[2];
+    u32x4 pf[RB];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x4 sc[2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sc[b] = mfma16(T.kf[b][ks], qf[ks], sc[b]);
+      for (int b = 0; b < 2; ++b) {
+        sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (kt + 8 * q4 + 4 * b + i > lim) sc[b][i] = -INFINITY;
+        for (int ks = 0; ks < KS; ++ks) sc[b] = mfma16(T.kf[b][ks], qf[rb][ks], sc[b]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kt + 8 * q4 + 4 * b + i > lim[rb]) sc[b][i] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[b][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[rb], mx * a.scale_log2);
+      if (mnew > m[rb]) {
+        const float alpha = __builtin_amdgcn_exp2f(m[rb] - mnew);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
+        l[rb] *= alpha;
+        m[rb] = mnew;
+      }
+      const float msafe = (m[rb] == -INFINITY) ? 0.f : m[rb];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[b][0], a.scale_log2, -msafe));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][1], a.scale_log2, -msafe));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[b][2], a.scale_log2, -msafe));
+        const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[b][3], a.scale_log2, -msafe));
+        l[rb] += (p0 + p1) + (p2 + p3);
+        pf[rb][2 * b] = pack2(p0, p1);
+        pf[rb][2 * b + 1] = pack2(p2, p3);
+      }
     }
-    float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int db = 0; db < DB; ++db) {
+      const u32x4 vv = clip_keys(T.vf[db], kt + 8 * q4, kv_len);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[b][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx * a.scale_log2);
-    if (mnew > m) {
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      l *= alpha;
-      m = mnew;
+      for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(vv, pf[rb], o[rb][db]);
     }
-    const float msafe = (m == -INFINITY) ? 0.f : m;
-    u32x4 pf;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[b][0], a.scale_log2, -msafe));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][1], a.scale_log2, -msafe));
-      const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[b][2], a.scale_log2, -msafe));
-      const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[b][3], a.scale_log2, -msafe));
-      l += (p0 + p1) + (p2 + p3);
-      pf[2 * b] = pack2(p0, p1);
-      pf[2 * b + 1] = pack2(p2, p3);
-    }
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = mfma16(clip_keys(T.vf[db], kt + 8 * q4, kv_len), pf, o[db]);
   };
 
-  // Two tiles in flight. Loads are issued whether or not the tile is used (tiles
-  // past the wave's range read the zero page): a load under a branch would make the
-  // compiler wait for it where the branches join.
-  Tile ta, tb;
-  load(tw0, ta);
-  for (int jj = tw0; jj < tw1; jj += 2) {
-    load(jj + 1, tb);
-    compute(ta);
-    load(jj + 2, ta);
-    if (jj + 1 < tw1) compute(tb);
+  if constexpr (RB == 1) {
+    // Two tiles in flight. Loads are issued whether or not the tile is used (tiles
+    // past the wave's range read the zero page): a load under a branch would make
+    // the compiler wait for it where the branches join.
+    Tile ta, tb;
+    load(tw0, ta);
+    for (int jj = tw0; jj < tw1; jj += 2) {
+      load(jj + 1, tb);
+      compute(ta);
+      load(jj + 2, ta);
+      if (jj + 1 < tw1) compute(tb);
+    }
+  } else {
+    Tile ta;
+    load(tw0, ta);
+    for (int jj = tw0; jj < tw1; ++jj) {
+      compute(ta);
+      load(jj + 1, ta);
+    }
   }
 
   // Merge the waves' partial results through LDS (the page's merge rule over the
   // kWaves parts): part[w][row][d] holds unnormalised o, mls[w][row] = (m, l).
-  float lt = l + __shfl_xor(l, 16);
-  lt += __shfl_xor(lt, 32);
+  constexpr int SR = RB * kSplitRows;  // rows per wave and rows of the partial slot
   float* part = reinterpret_cast<float*>(smem);
-  float* mls = part + kWaves * kSplitRows * D;
-  if (valid) {
+  float* mls = part + kWaves * SR * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<float4*>(part + (wave * kSplitRows + l16) * D + db * 16 + 4 * q4) =
-          float4{o[db][0], o[db][1], o[db][2], o[db][3]};
-    if (q4 == 0) {
-      mls[(wave * kSplitRows + l16) * 2] = m;
-      mls[(wave * kSplitRows + l16) * 2 + 1] = lt;
+  for (int rb = 0; rb < RB; ++rb) {
+    float lt = l[rb] + __shfl_xor(l[rb], 16);
+    lt += __shfl_xor(lt, 32);
+    const int rr = rb * kSplitRows + l16;
+    if (rr < it.nrows) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<float4*>(part + (wave * SR + rr) * D + db * 16 + 4 * q4) =
+            float4{o[rb][db][0], o[rb][db][1], o[rb][db][2], o[rb][db][3]};
+      if (q4 == 0) {
+        mls[(wave * SR + rr) * 2] = m[rb];
+        mls[(wave * SR + rr) * 2 + 1] = lt;
+      }
     }
   }
   __syncthreads();
-  constexpr int TPR = D / 4;  // threads per row, 4 features each
-  static_assert(kThreads / TPR >= kSplitRows, "one pass must cover the rows");
-  const int r = tid / TPR, c4 = (tid % TPR) * 4;
-  const bool act = r < it.nrows;
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f, M = -INFINITY;
-  if (act) {
+  constexpr int TPR = D / 4;           // threads per row, 4 features each
+  constexpr int RPP = kThreads / TPR;  // rows per pass
+  const int c4 = (tid % TPR) * 4;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mls[(w * kSplitRows + r) * 2]);
+  for (int r0 = 0; r0 < SR; r0 += RPP) {
+    const int r = r0 + tid / TPR;
+    if (r >= it.nrows) continue;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f, M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mls[(w * SR + r) * 2]);
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float lw = mls[(w * kSplitRows + r) * 2 + 1];
+        const float lw = mls[(w * SR + r) * 2 + 1];
         if (lw > 0.f) {
-          const float f = __builtin_amdgcn_exp2f(mls[(w * kSplitRows + r) * 2] - M);
-          const float4 ow = *reinterpret_cast<const float4*>(part + (w * kSplitRows + r) * D + c4);
+          const float f = __builtin_amdgcn_exp2f(mls[(w * SR + r) * 2] - M);
+          const float4 ow = *reinterpret_cast<const float4*>(part + (w * SR + r) * D + c4);
           L += f * lw;
           acc.x += f * ow.x;
           acc.y += f * ow.y;
@@ -747,27 +786,23 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
         }
       }
     }
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  const float lse_wg = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
-  const int rpos = act ? r / G : 0;
-  const int64_t orow_r = int64_t(si.q_off + rpos) * a.hq + g * G + (act ? r - rpos * G : 0);
-  auto store_out = [&](float4 v, float lse_v) {
-    uint16_t* op = static_cast<uint16_t*>(a.out) + orow_r * D + c4;
-    u32x2 pk = {pack2(v.x, v.y), pack2(v.z, v.w)};
-    *reinterpret_cast<u32x2*>(op) = pk;
-    if (c4 == 0 && a.lse) a.lse[orow_r] = lse_v;
-  };
-  if (it.task < 0) {  // this workgroup covered the whole key range
-    if (act) store_out(float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv}, lse_wg);
-    return;
-  }
-  // Leave this workgroup's partial (normalised o, natural-log lse) in its slot; the
-  // combine kernel merges the workgroups' partials of the task.
-  float* sl = a.slots + it.slot;  // rows [kSplitRows][D], then lse [kSplitRows]
-  if (act) {
-    *reinterpret_cast<float4*>(sl + r * D + c4) = float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
-    if (c4 == 0) sl[kSplitRows * D + r] = lse_wg;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float lse_wg = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+    const float4 res = float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    if (it.task < 0) {  // this workgroup covered the whole key range
+      const int rpos = r / G;
+      const int64_t orow_r = int64_t(si.q_off + rpos) * a.hq + g * G + (r - rpos * G);
+      uint16_t* op = static_cast<uint16_t*>(a.out) + orow_r * D + c4;
+      u32x2 pk = {pack2(res.x, res.y), pack2(res.z, res.w)};
+      *reinterpret_cast<u32x2*>(op) = pk;
+      if (c4 == 0 && a.lse) a.lse[orow_r] = lse_wg;
+    } else {
+      // Leave this workgroup's partial (normalised o, natural-log lse) in its slot;
+      // the combine kernel merges the workgroups' partials of the task.
+      float* sl = a.slots + it.slot;  // rows [SR][D], then lse [SR]
+      *reinterpret_cast<float4*>(sl + r * D + c4) = res;
+      if (c4 == 0) sl[SR * D + r] = lse_wg;
+    }
   }
 }
 
@@ -775,13 +810,15 @@ template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr int kChunkLds = 2 * 4 * kChunkKeys * D * 2 + 512;                     // K/V rings + block ids
-  constexpr int kSplitLds = kWaves * kSplitRows * (D + 2) * 4;                     // wave partials
+  constexpr int kSplitLds = kWaves * 2 * kSplitRows * (D + 2) * 4;                 // wave partials (2 row blocks)
   __shared__ __attribute__((aligned(16))) unsigned char smem[kChunkLds > kSplitLds ? kChunkLds : kSplitLds];
   const WorkItem it = a.items[blockIdx.x];
   if (it.kind == kItemChunk)
     chunk_item<D>(a, it, smem);
+  else if (it.nrows <= kSplitRows)
+    split_item<D, 1>(a, it, smem);
   else
-    split_item<D>(a, it, smem);
+    split_item<D, 2>(a, it, smem);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {

@@ -22,7 +22,8 @@ constexpr int kSplitTargetItems = 512;  // split path aims at this many workgrou
 constexpr int kChunkTargetItems = 256;  // chunk rows: split key ranges until about this many workgroups (1 per CU)
 constexpr int kChunkMinPieceKeys = 2048;  // ... with at least this many keys per piece
 constexpr int kCombineRows = 32;         // rows per combine task of split chunk tiles
-constexpr int kSplitRows = 16;    // split path: at most this many rows (one 16-row MFMA block)
+constexpr int kSplitRows = 16;    // split path: rows of one 16-row MFMA block
+constexpr int kSplitMaxRows = 32; // split path: at most this many rows (two blocks per wave)
 
 // Per-request metadata copied to the workspace.
 struct SeqInfo {
@@ -34,7 +35,7 @@ struct SeqInfo {
 
 enum : int32_t {
   kItemChunk = 0,  // kRowsPerTile rows of one (request, KV head); all waves share LDS K/V tiles
-  kItemSplit = 1,  // <= 16 rows; each wave takes its own part of the key range
+  kItemSplit = 1,  // <= kSplitMaxRows rows; each wave takes its own part of the key range
 };
 
 // One workgroup's work. Rows are flattened per (request, KV head) as
@@ -44,7 +45,7 @@ struct WorkItem {
   int32_t seq;
   int32_t kv_head;
   int32_t row0;       // first flattened row
-  int32_t nrows;      // rows in this item (<= kRowsPerTile chunk, <= kSplitRows split)
+  int32_t nrows;      // rows in this item (<= kRowsPerTile chunk, <= kSplitMaxRows split)
   int32_t key_begin;  // keys [key_begin, key_end); key_begin is a multiple of kChunkKeys
   int32_t key_end;
   int32_t slot;       // < 0: write out/lse directly; else float offset of this item's partial slot

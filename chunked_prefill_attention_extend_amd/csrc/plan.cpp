@@ -40,9 +40,9 @@ int chunk_plan_impl(int64_t n_tokens, int64_t chunk_size, double hit_rate, int64
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Work list of one launch. Requests whose E * group rows fit one 16-row MFMA
-// block (decode rows, short verify rows) take the split path: the key range is cut into
-// pieces (one workgroup each, one part per wave); each workgroup
+// Work list of one launch. Requests whose E * group rows fit two 16-row MFMA
+// blocks (decode rows, multi-token verify rows) take the split path: the key range
+// is cut into pieces (one workgroup each, one part per wave); each workgroup
 // merges its waves' parts and leaves one partial result, and the combine kernel
 // merges the workgroups' partials. Longer chunks take the chunk path:
 // kRowsPerTile-row tiles over their whole causal key range.
@@ -69,7 +69,7 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
     // of kWaves tiles, between kSplitKeysMin and kSplitKeysMax.
     int64_t split_keys = 0;
     for (int32_t r = 0; r < num_seqs; ++r)
-      if (int64_t(extend[r]) * group <= kSplitRows) split_keys += (int64_t(prefix[r]) + extend[r]) * hkv;
+      if (int64_t(extend[r]) * group <= kSplitMaxRows) split_keys += (int64_t(prefix[r]) + extend[r]) * hkv;
     constexpr int64_t kGrain = int64_t(kSplitTile) * kWaves;
     int64_t piece = (split_keys + kSplitTargetItems - 1) / kSplitTargetItems;
     piece = (piece + kGrain - 1) / kGrain * kGrain;
@@ -82,16 +82,17 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
     int64_t chunk_tiles = 0;
     for (int32_t r = 0; r < num_seqs; ++r) {
       const int64_t rows = int64_t(extend[r]) * group;
-      if (rows > kSplitRows) chunk_tiles += (rows + kRowsPerTile - 1) / kRowsPerTile * hkv;
+      if (rows > kSplitMaxRows) chunk_tiles += (rows + kRowsPerTile - 1) / kRowsPerTile * hkv;
     }
     const int64_t chunk_pieces =
         chunk_tiles > 0 ? std::max<int64_t>(1, (kChunkTargetItems + chunk_tiles - 1) / chunk_tiles) : 1;
     for (int32_t r = 0; r < num_seqs; ++r) {
       const int64_t rows = int64_t(extend[r]) * group;
       const int64_t kv_len = int64_t(prefix[r]) + extend[r];
-      if (rows <= kSplitRows) {
+      if (rows <= kSplitMaxRows) {
+        const int32_t srows = rows <= kSplitRows ? kSplitRows : kSplitMaxRows;  // rows of a partial slot
         const int64_t nwg = (kv_len + piece - 1) / piece;
-        const int64_t sf = int64_t(slot_floats(kSplitRows, head_dim));
+        const int64_t sf = int64_t(slot_floats(srows, head_dim));
         for (int32_t g = 0; g < hkv; ++g) {
           const int64_t slot0 = plan.n_slot_floats;
           const int32_t task = nwg > 1 ? int32_t(plan.tasks.size()) : -1;
@@ -103,7 +104,7 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
           }
           if (nwg > 1) {
             plan.tasks.push_back(CombineTask{r, g, 0, int32_t(rows), int32_t(slot0), int32_t(nwg), int32_t(sf),
-                                             kSplitRows, 0, {0, 0, 0}});
+                                             srows, 0, {0, 0, 0}});
             plan.n_slot_floats += nwg * sf;
           }
         }
