@@ -172,6 +172,19 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
     for i in dec:
         L = prefix[i] + 1
         dec_bytes += 2 * L * hkv * d * 2 + 2 * hq * d * 2 + 4 * hq + 4 * math.ceil(L / 16)
+    # Inside the full mixed launch: per-workgroup wall-clock stamps (measurement
+    # variant of the same launch), decode span = first decode workgroup start to
+    # last decode workgroup end (the combine kernel after it is not included).
+    spans = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        _, st, hz = ext.extend_attention(q, k_cache, v_cache, bt, prefix, extend, w.scale, out, lse, workspace=ws,
+                                         timed=True)
+        st = st.cpu().numpy()
+        dsel, csel = st[:, 2] == 1, st[:, 2] == 0
+        spans.append(((st[dsel, 1].max() - st[dsel, 0].min()) / hz, (st[csel, 1].max() - st[csel, 0].min()) / hz,
+                      (st[:, 1].max() - st[:, 0].min()) / hz))
+    dspan, cspan, kspan = (float(np.median([x[j] for x in spans])) for j in range(3))
     chunk = [(p, e) for p, e in zip(prefix, extend) if e > 1]
     chunk_flops = sweep_flops(chunk, hq, d)
     return {
@@ -185,6 +198,12 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
         "decode_bytes": dec_bytes,
         "decode_GBps": dec_bytes / t_dec / 1e9,
         "decode_frac_hbm_peak": dec_bytes / t_dec / 1e9 / PEAK_HBM_GBS,
+        "decode_span_in_mixed_ms": dspan * 1e3,
+        "decode_GBps_in_mixed": dec_bytes / dspan / 1e9,
+        "decode_frac_hbm_peak_in_mixed": dec_bytes / dspan / 1e9 / PEAK_HBM_GBS,
+        "chunk_span_in_mixed_ms": cspan * 1e3,
+        "attention_kernel_span_ms": kspan * 1e3,
+        "span_note": "per-workgroup wall-clock stamps (measurement variant of the same launch), median of %d" % reps,
         "chunk_flops": chunk_flops,
         "mixed_lower_bound_ms": max(chunk_flops / (PEAK_BF16_TFLOPS * 1e12), dec_bytes / (PEAK_HBM_GBS * 1e9)) * 1e3,
     }
@@ -439,6 +458,10 @@ def main() -> int:
     if not args.no_mixed:
         log("mixed step")
         mixed = mixed_step_bench(torch, ext, synth)
+    verify = None
+    if not args.no_mixed:
+        log("verify rows")
+        verify = verify_rows_sweep(torch, ext, synth)
     log("calibration")
     calib = calibration(torch)
     base = None
@@ -470,6 +493,7 @@ def main() -> int:
                             "note": "attention launches only (kv_append excluded); sum(F) / sum(per-chunk median)"},
         "calibration": calib,
         "mixed_step": mixed,
+        "verify_rows": verify,
         "cpu_baseline": base,
     }
     print(json.dumps(line), flush=True)

@@ -70,6 +70,9 @@ def load_library() -> ctypes.CDLL:
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.extattn_extend_attention_timed.restype = ctypes.c_int
+    lib.extattn_extend_attention_timed.argtypes = [*lib.extattn_extend_attention.argtypes, ctypes.c_void_p,
+                                                   ctypes.c_int32, _c_i32p, ctypes.POINTER(ctypes.c_double)]
     _lib = lib
     return lib
 
@@ -272,12 +275,14 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, prefix_lens, extend_l
 
 
 def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale: float, out,
-                     lse=None, workspace=None, stream=None):
+                     lse=None, workspace=None, stream=None, timed: bool = False):
     """Chunked-prefill extend attention over the paged cache.
 
     q, out: device ``[sum(E), Hq, D]``; lse: device float32 ``[sum(E), Hq]`` or None;
     prefix_lens / extend_lens: host, one entry per block_table row.
-    Returns ``out``.
+    Returns ``out``; with ``timed`` (bf16 only) the measurement variant runs and
+    ``(out, stamps, tick_hz)`` is returned, ``stamps`` a device int64 ``[items, 4]``
+    of {start, end, kind (0 chunk, 1 decode / verify), request} per work item.
     """
     import torch
     lib = load_library()
@@ -299,9 +304,19 @@ def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens,
     code = _dtype_code(q)
     need = workspace_bytes(p, e, hq, hkv, d, code)
     ws = _workspace(need, q.device, workspace)
-    _check(lib.extattn_extend_attention(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                        block_table.data_ptr(), block_table.shape[1], nb, _ptr(p), _ptr(e),
-                                        len(p), hq, hkv, d, bs, float(scale), code, out.data_ptr(),
-                                        lse.data_ptr() if lse is not None else None, ws.data_ptr(),
-                                        ws.numel() * ws.element_size(), _stream_handle(stream)))
-    return out
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1], nb,
+            _ptr(p), _ptr(e), len(p), hq, hkv, d, bs, float(scale), code, out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, ws.data_ptr(), ws.numel() * ws.element_size(),
+            _stream_handle(stream))
+    if not timed:
+        _check(lib.extattn_extend_attention(*args))
+        return out
+    n = ctypes.c_int32(0)
+    hz = ctypes.c_double(0.0)
+    rc = lib.extattn_extend_attention_timed(*args, None, 0, ctypes.byref(n), ctypes.byref(hz))
+    if rc != EXTATTN_ENOSPC or n.value < 1:
+        _check(rc)
+        raise RuntimeError("timed launch: no work items")
+    stamps = torch.empty((n.value, 4), dtype=torch.int64, device=q.device)
+    _check(lib.extattn_extend_attention_timed(*args, stamps.data_ptr(), n.value, ctypes.byref(n), ctypes.byref(hz)))
+    return out, stamps, hz.value

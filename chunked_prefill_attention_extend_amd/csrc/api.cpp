@@ -248,12 +248,18 @@ int extattn_kv_append(const void* k_new, const void* v_new, void* k_cache, void*
   return EXTATTN_OK;
 }
 
-int extattn_extend_attention(const void* q, const void* k_cache, const void* v_cache,
-                             const int32_t* block_table, int32_t max_blocks, int64_t num_blocks,
-                             const int32_t* prefix_lens, const int32_t* extend_lens, int32_t num_seqs,
-                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                             int32_t block_size, float scale, int32_t dtype, void* out, float* lse,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks, planning, metadata upload and launches of one extend-attention call;
+// with `timed`, the attention kernel records per-item wall-clock stamps.
+int extend_call(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                int32_t max_blocks, int64_t num_blocks, const int32_t* prefix_lens, const int32_t* extend_lens,
+                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                int32_t block_size, float scale, int32_t dtype, void* out, float* lse, void* workspace,
+                size_t workspace_bytes, void* stream, bool timed, int64_t* stamps, int32_t capacity,
+                int32_t* n_items, double* tick_hz) {
   int rc = check_common(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, true);
   if (rc != EXTATTN_OK) return rc;
   rc = check_blocks(num_seqs, prefix_lens, extend_lens, max_blocks, num_blocks, block_size);
@@ -266,6 +272,18 @@ int extattn_extend_attention(const void* q, const void* k_cache, const void* v_c
   rc = build_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, plan);
   if (rc != EXTATTN_OK) return fail(rc, "planning failed");
   if (workspace_bytes < plan.bytes) return fail(EXTATTN_ENOSPC, "workspace too small");
+  if (timed) {
+    if (!n_items || !tick_hz) return fail(EXTATTN_EINVAL, "null n_items or tick_hz");
+    if (dtype != EXTATTN_BF16) return fail(EXTATTN_EUNSUPPORTED, "timed launches exist for bf16 only");
+    *n_items = int32_t(plan.items.size());
+    int dev = 0, khz = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he == hipSuccess) he = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (he != hipSuccess) return hip_fail(he, "wall clock rate");
+    *tick_hz = double(khz) * 1e3;
+    if (capacity < *n_items) return fail(EXTATTN_ENOSPC, "stamp capacity is smaller than the number of work items");
+    if (!stamps) return fail(EXTATTN_EINVAL, "null stamps");
+  }
 
   std::vector<unsigned char> blob(plan.upload_bytes, 0);
   std::memcpy(blob.data() + plan.off_seqs, plan.seqs.data(), sizeof(SeqInfo) * plan.seqs.size());
@@ -303,6 +321,7 @@ int extattn_extend_attention(const void* q, const void* k_cache, const void* v_c
   a.total_rows = int32_t(plan.total_rows);
   a.n_items = int32_t(plan.items.size());
   a.n_tasks = int32_t(plan.tasks.size());
+  a.stamps = timed ? stamps : nullptr;
 
   hipError_t e;
   if (dtype == EXTATTN_F32) {
@@ -320,6 +339,33 @@ int extattn_extend_attention(const void* q, const void* k_cache, const void* v_c
   }
   g_error.clear();
   return EXTATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int extattn_extend_attention(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, int32_t max_blocks, int64_t num_blocks,
+                             const int32_t* prefix_lens, const int32_t* extend_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, float scale, int32_t dtype, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return extend_call(q, k_cache, v_cache, block_table, max_blocks, num_blocks, prefix_lens, extend_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, scale, dtype, out, lse, workspace,
+                     workspace_bytes, stream, false, nullptr, 0, nullptr, nullptr);
+}
+
+int extattn_extend_attention_timed(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, int32_t max_blocks, int64_t num_blocks,
+                                   const int32_t* prefix_lens, const int32_t* extend_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, float scale, int32_t dtype, void* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream, int64_t* stamps,
+                                   int32_t capacity, int32_t* n_items, double* tick_hz) {
+  return extend_call(q, k_cache, v_cache, block_table, max_blocks, num_blocks, prefix_lens, extend_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, scale, dtype, out, lse, workspace,
+                     workspace_bytes, stream, true, stamps, capacity, n_items, tick_hz);
 }
 
 }  // extern "C"

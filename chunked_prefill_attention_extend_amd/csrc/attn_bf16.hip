@@ -813,12 +813,24 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int kSplitLds = kWaves * 2 * kSplitRows * (D + 2) * 4;                 // wave partials (2 row blocks)
   __shared__ __attribute__((aligned(16))) unsigned char smem[kChunkLds > kSplitLds ? kChunkLds : kSplitLds];
   const WorkItem it = a.items[blockIdx.x];
+  // measurement variant: the workgroup's start and end (after its last wave) in
+  // wall-clock ticks; the start is stored at once so that nothing stays live
+  if (a.stamps && threadIdx.x == 0) {
+    int64_t* st = a.stamps + 4 * int64_t(blockIdx.x);
+    st[0] = int64_t(wall_clock64());
+    st[2] = it.kind;
+    st[3] = it.seq;
+  }
   if (it.kind == kItemChunk)
     chunk_item<D>(a, it, smem);
   else if (it.nrows <= kSplitRows)
     split_item<D, 1>(a, it, smem);
   else
     split_item<D, 2>(a, it, smem);
+  if (a.stamps) {
+    __syncthreads();
+    if (threadIdx.x == 0) a.stamps[4 * int64_t(blockIdx.x) + 1] = int64_t(wall_clock64());
+  }
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {

@@ -22,6 +22,7 @@ constexpr int kSplitTargetItems = 512;  // split path aims at this many workgrou
 constexpr int kChunkTargetItems = 256;  // chunk rows: split key ranges until about this many workgroups (1 per CU)
 constexpr int kChunkMinPieceKeys = 2048;  // ... with at least this many keys per piece
 constexpr int kCombineRows = 32;         // rows per combine task of split chunk tiles
+constexpr int kXcds = 8;  // accelerator dies (own L2 each); a launch's workgroups are dealt to them round-robin
 constexpr int kSplitRows = 16;    // split path: rows of one 16-row MFMA block
 constexpr int kSplitMaxRows = 32; // split path: at most this many rows (two blocks per wave)
 
@@ -97,6 +98,7 @@ struct AttnArgs {
   int32_t total_rows;
   int32_t n_items;
   int32_t n_tasks;
+  int64_t* stamps;   // NULL, or [n_items][4] {start, end, kind, request} in wall-clock ticks
 };
 
 struct KvArgs {

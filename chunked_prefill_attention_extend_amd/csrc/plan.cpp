@@ -1,8 +1,10 @@
 // Host-side planning: the chunk plan of one prompt and the work list of one
 // extend-attention launch.
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdint>
+#include <map>
 
 #include "../../include/extattn.h"
 #include "internal.hpp"
@@ -40,6 +42,95 @@ int chunk_plan_impl(int64_t n_tokens, int64_t chunk_size, double hit_rate, int64
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Lead of the chunk items over the split items in the launch order (percent of the
+// split work): see the interleave in build_plan.
+constexpr int64_t kChunkLeadPct = 30;
+
+// Launch order of the work items. Workgroups are dealt round-robin to the kXcds
+// accelerator dies (workgroup b to die b % kXcds, each die with its own L2) and
+// dispatched in order within a die, so the list is built as kXcds lanes, one per
+// die, read out round-robin:
+//  * each chunk group (tiles sharing one K/V range) goes whole to one lane, the
+//    longest groups first to the lane with the least chunk work, its tiles
+//    consecutive so that they run side by side and read the K/V into L2 once;
+//  * split items (decode / verify rows), longest first, fill the lanes to equal
+//    item counts, each to the lane with the most room and then the least work;
+//  * within a lane the chunk and split items are interleaved so that both kinds
+//    advance through their work at the same rate: chunk rows (matrix-core bound)
+//    and decode rows (HBM bound) then run side by side on different CUs from the
+//    start instead of the decode rows waiting for the chunk rows' CUs. The chunk
+//    items run ahead by kChunkLeadPct percent of the split work, so that the long
+//    chunk items are all under way while short split items remain for the end.
+// Work is estimated as rows x keys for a chunk item and keys for a split item.
+static void order_items(std::vector<std::vector<WorkItem>>& groups, std::vector<WorkItem>& split_items,
+                        std::vector<WorkItem>& out) {
+  auto chunk_work = [](const WorkItem& x) { return int64_t(x.key_end - x.key_begin) * x.nrows; };
+  auto split_work = [](const WorkItem& x) { return int64_t(x.key_end - x.key_begin); };
+  struct Lane {
+    std::vector<WorkItem> chunk, split;
+    int64_t cwork = 0, swork = 0;
+  };
+  std::vector<Lane> lanes(kXcds);
+  std::vector<int64_t> gwork(groups.size(), 0);
+  for (size_t i = 0; i < groups.size(); ++i) {
+    std::stable_sort(groups[i].begin(), groups[i].end(),
+                     [&](const WorkItem& x, const WorkItem& y) { return chunk_work(x) > chunk_work(y); });
+    for (const WorkItem& x : groups[i]) gwork[i] += chunk_work(x);
+  }
+  std::vector<size_t> gorder(groups.size());
+  for (size_t i = 0; i < gorder.size(); ++i) gorder[i] = i;
+  std::stable_sort(gorder.begin(), gorder.end(), [&](size_t a, size_t b) { return gwork[a] > gwork[b]; });
+  size_t n_total = split_items.size();
+  for (size_t gi : gorder) {
+    size_t best = 0;
+    for (size_t l = 1; l < lanes.size(); ++l)
+      if (lanes[l].cwork < lanes[best].cwork ||
+          (lanes[l].cwork == lanes[best].cwork && lanes[l].chunk.size() < lanes[best].chunk.size()))
+        best = l;
+    lanes[best].chunk.insert(lanes[best].chunk.end(), groups[gi].begin(), groups[gi].end());
+    lanes[best].cwork += gwork[gi];
+    n_total += groups[gi].size();
+  }
+  std::stable_sort(split_items.begin(), split_items.end(),
+                   [&](const WorkItem& x, const WorkItem& y) { return split_work(x) > split_work(y); });
+  const int64_t target = int64_t((n_total + lanes.size() - 1) / lanes.size());
+  for (const WorkItem& x : split_items) {
+    size_t best = 0;
+    auto room = [&](size_t l) { return target - int64_t(lanes[l].chunk.size() + lanes[l].split.size()); };
+    for (size_t l = 1; l < lanes.size(); ++l)
+      if (room(l) > room(best) || (room(l) == room(best) && lanes[l].swork < lanes[best].swork)) best = l;
+    lanes[best].split.push_back(x);
+    lanes[best].swork += split_work(x);
+  }
+  // interleave within each lane
+  std::vector<std::vector<WorkItem>> seq(lanes.size());
+  for (size_t l = 0; l < lanes.size(); ++l) {
+    const Lane& ln = lanes[l];
+    size_t ci = 0, si = 0;
+    int64_t cdone = 0, sdone = 0;
+    while (ci < ln.chunk.size() || si < ln.split.size()) {
+      // next item from the list whose dispatched fraction (with the chunk lead) is smaller
+      const bool take_chunk =
+          si == ln.split.size() ||
+          (ci < ln.chunk.size() &&
+           __int128(cdone) * ln.swork * (100 - kChunkLeadPct) <= __int128(sdone) * ln.cwork * 100);
+      if (take_chunk) {
+        cdone += chunk_work(ln.chunk[ci]);
+        seq[l].push_back(ln.chunk[ci++]);
+      } else {
+        sdone += split_work(ln.split[si]);
+        seq[l].push_back(ln.split[si++]);
+      }
+    }
+  }
+  // read the lanes out round-robin
+  out.clear();
+  out.reserve(n_total);
+  for (size_t k = 0; out.size() < n_total; ++k)
+    for (size_t l = 0; l < seq.size(); ++l)
+      if (k < seq[l].size()) out.push_back(seq[l][k]);
+}
+
 // Work list of one launch. Requests whose E * group rows fit two 16-row MFMA
 // blocks (decode rows, multi-token verify rows) take the split path: the key range
 // is cut into pieces (one workgroup each, one part per wave); each workgroup
@@ -62,7 +153,20 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
   plan.total_rows = q_off;
 
   if (dtype == EXTATTN_BF16) {
-    std::vector<WorkItem> chunk_items, split_items;
+    std::vector<WorkItem> split_items;
+    // Chunk items by group: the tiles of one (request, KV head, key piece) read the
+    // same K/V range, so they are launched side by side on one XCD (shared L2).
+    std::vector<std::vector<WorkItem>> groups;
+    std::map<std::array<int64_t, 3>, size_t> group_of;
+    auto add_chunk = [&](const WorkItem& x, int64_t piece_index) {
+      const std::array<int64_t, 3> key{x.seq, x.kv_head, piece_index};
+      auto f = group_of.find(key);
+      if (f == group_of.end()) {
+        f = group_of.emplace(key, groups.size()).first;
+        groups.emplace_back();
+      }
+      groups[f->second].push_back(x);
+    };
     // Keys per split workgroup: every workgroup pays a fixed start-up (ids, first
     // loads in flight) while it holds its CU alone, so pieces are as long as the
     // work allows while still giving about kSplitTargetItems workgroups; a multiple
@@ -120,8 +224,9 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
             const int64_t ktiles = (key_end + kChunkKeys - 1) / kChunkKeys;
             const int64_t pieces = std::max<int64_t>(1, std::min<int64_t>(chunk_pieces, key_end / kChunkMinPieceKeys));
             if (pieces == 1) {
-              chunk_items.push_back(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), 0,
-                                             int32_t(key_end), -1, -1, {0, 0, 0}});
+              add_chunk(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), 0, int32_t(key_end), -1, -1,
+                                 {0, 0, 0}},
+                        0);
               continue;
             }
             // pieces of about equal tile counts; the last one holds the diagonal
@@ -130,8 +235,9 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
             for (int64_t i = 0; i < pieces; ++i) {
               const int64_t kb = ktiles * i / pieces * kChunkKeys;
               const int64_t ke = i + 1 < pieces ? ktiles * (i + 1) / pieces * kChunkKeys : key_end;
-              chunk_items.push_back(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), int32_t(kb),
-                                             int32_t(ke), int32_t(slot0 + i * sf), task0, {0, 0, 0}});
+              add_chunk(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), int32_t(kb), int32_t(ke),
+                                 int32_t(slot0 + i * sf), task0, {0, 0, 0}},
+                        i);
             }
             for (int64_t sr = 0; sr < nrows; sr += kCombineRows)
               plan.tasks.push_back(CombineTask{r, g, int32_t(row0 + sr),
@@ -142,15 +248,7 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
         }
       }
     }
-    // Longest chunk tiles first (they set the makespan), then the split work.
-    std::stable_sort(chunk_items.begin(), chunk_items.end(), [](const WorkItem& x, const WorkItem& y) {
-      return int64_t(x.key_end - x.key_begin) * x.nrows > int64_t(y.key_end - y.key_begin) * y.nrows;
-    });
-    std::stable_sort(split_items.begin(), split_items.end(), [](const WorkItem& x, const WorkItem& y) {
-      return (x.key_end - x.key_begin) > (y.key_end - y.key_begin);
-    });
-    plan.items = std::move(chunk_items);
-    plan.items.insert(plan.items.end(), split_items.begin(), split_items.end());
+    order_items(groups, split_items, plan.items);
   }
 
   size_t off = kHeaderBytes;

@@ -235,6 +235,36 @@ int extattn_extend_attention(const void* q, const void* k_cache, const void* v_c
                              void* out, float* lse, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * Measurement variant of extattn_extend_attention: the same work and the same
+ * results, and each workgroup of the bf16 attention kernel (one work item: a
+ * chunk tile, a piece of one, or a piece of a decode / verify request's key
+ * range) also records when it started and ended. This gives the span of the
+ * decode rows inside a mixed launch (the mixed chunk-and-decode step of the
+ * token-budget blog, section 5) next to the chunk rows' span.
+ *
+ * Arguments as for extattn_extend_attention, plus:
+ * stamps:   device int64 [capacity][4]; item i writes {start, end, kind,
+ *           request}: start / end in ticks of the device's constant-rate wall
+ *           clock, kind 0 for chunk rows and 1 for decode / verify rows, request
+ *           the index into prefix_lens. Items are in launch order. The combine
+ *           kernel that follows split items is not recorded.
+ * capacity: number of 4-entry records stamps can hold; 0 (stamps NULL) asks
+ *           only for n_items and returns EXTATTN_ENOSPC without enqueuing work.
+ * n_items:  host out: the launch's number of work items.
+ * tick_hz:  host out: wall-clock ticks per second of the current device.
+ * Errors: those of extattn_extend_attention; EXTATTN_ENOSPC when capacity <
+ * n_items; EXTATTN_EUNSUPPORTED for fp32 (its kernel records nothing).
+ */
+int extattn_extend_attention_timed(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, int32_t max_blocks, int64_t num_blocks,
+                                   const int32_t* prefix_lens, const int32_t* extend_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, float scale, int32_t dtype,
+                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream, int64_t* stamps, int32_t capacity, int32_t* n_items,
+                                   double* tick_hz);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char* extattn_last_error(void);
 

@@ -91,6 +91,34 @@ def test_verify_rows_long_contexts():
     check_launch(sub, out, lse, q_off, q, what="verify rows, long contexts")
 
 
+def test_timed_variant_same_results_and_sane_stamps():
+    """The measurement variant gives bit-identical results and one
+    {start, end, kind, request} record per work item."""
+    launches = [(3000, 1), (900, 600), (4000, 5), (12, 1)]
+    w = custom_workload(61, launches, 32, 8, 128)
+    log("timed variant: mixed launch of decode, verify and chunk rows")
+    out, lse, q_off, q = run_launch(w)
+    cache = PagedCache(w)
+    for r in w.requests:
+        p, e = r.launch
+        cache.append([r.index], [0], w.k(r, 0, p + e), w.v(r, 0, p + e), [p + e])
+    qd = dev_tensor(q, w.dtype)
+    o2 = torch.empty_like(qd)
+    l2 = torch.empty_like(lse)
+    prefix = [p for p, _ in launches]
+    extend = [e for _, e in launches]
+    _, st, hz = ext.extend_attention(qd, cache.k, cache.v, cache.bt, prefix, extend, w.scale, o2, l2, timed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2), "timed launch changed the results"
+    st = st.cpu().numpy()
+    assert hz > 0 and st.shape[1] == 4 and st.shape[0] > 0
+    assert (st[:, 1] >= st[:, 0]).all() and (st[:, 0] > 0).all()
+    assert set(st[:, 2].tolist()) == {0, 1}
+    kinds = {int(r): int(k) for k, r in zip(st[:, 2], st[:, 3])}
+    assert kinds == {0: 1, 1: 0, 2: 1, 3: 1}, kinds   # rows per KV head: 4, 2400, 20, 4
+    assert (st[:, 1].max() - st[:, 0].min()) / hz < 1.0
+
+
 def test_fp32_mixed_and_gqa():
     w = custom_workload(7, [(50, 30), (129, 1), (0, 70)], 8, 2, 128, dtype="f32", mult=1.0)
     log("fp32 mixed launch with GQA")
