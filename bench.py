@@ -99,10 +99,20 @@ def setup_sweep(torch, ext, synth):
                 out=out, lse=lse, ws=ws, kv_ws=kv_ws, scale=w.scale)
 
 
-def sweep_step(ext, s, events=None):
+def sweep_step(ext, s, events=None, fused=False):
     """One pass over the 128 chunks. ``events``: list of (start, end) pairs
-    recorded around each extend_attention call."""
+    recorded around each extend_attention call. ``fused``: each chunk's K/V
+    append runs inside its attention launch (extend_attention_append)."""
     for t, (p, e) in enumerate(s["plan"]):
+        if fused:
+            if events is not None:
+                events[t][0].record()
+            ext.extend_attention_append(s["q"][p:p + e], s["k_new"][p:p + e], s["v_new"][p:p + e], s["k_cache"],
+                                        s["v_cache"], s["bt"], [p], [e], s["scale"], s["out"][p:p + e],
+                                        s["lse"][p:p + e], workspace=s["ws"])
+            if events is not None:
+                events[t][1].record()
+            continue
         ext.kv_append(s["k_new"][p:p + e], s["v_new"][p:p + e], s["k_cache"], s["v_cache"], s["bt"], [p], [e],
                       workspace=s["kv_ws"])
         if events is not None:
@@ -454,6 +464,19 @@ def main() -> int:
     ms = dt / args.steps * 1e3
     value = flops / (dt / args.steps) / 1e12
 
+    # The same steps with each chunk's append fused into its attention launch.
+    for i in range(args.warmup):
+        sweep_step(ext, s, fused=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        sweep_step(ext, s, fused=True)
+    torch.cuda.synchronize()
+    dtf = time.perf_counter() - t0
+    fused = {"ms_per_step": dtf / args.steps * 1e3, "tflops": flops / (dtf / args.steps) / 1e12,
+             "note": "128 x extend_attention_append (append inside the attention launch)"}
+    log(f"fused steps: {dtf / args.steps * 1e3:.1f} ms per step")
+
     mixed = None
     if not args.no_mixed:
         log("mixed step")
@@ -492,6 +515,7 @@ def main() -> int:
         "sweep_attention": {"aggregate_tflops": aggregate, "per_chunk_tflops": per_chunk,
                             "note": "attention launches only (kv_append excluded); sum(F) / sum(per-chunk median)"},
         "calibration": calib,
+        "fused_append_step": fused,
         "mixed_step": mixed,
         "verify_rows": verify,
         "cpu_baseline": base,

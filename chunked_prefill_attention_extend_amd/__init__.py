@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     chunk_plan,
     decode_first_with_slack,
     extend_attention,
+    extend_attention_append,
     kv_append,
     load_library,
     mixed_chunk_step,

@@ -70,6 +70,9 @@ def load_library() -> ctypes.CDLL:
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.extattn_extend_attention_append.restype = ctypes.c_int
+    lib.extattn_extend_attention_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                    *lib.extattn_extend_attention.argtypes[1:]]
     lib.extattn_extend_attention_timed.restype = ctypes.c_int
     lib.extattn_extend_attention_timed.argtypes = [*lib.extattn_extend_attention.argtypes, ctypes.c_void_p,
                                                    ctypes.c_int32, _c_i32p, ctypes.POINTER(ctypes.c_double)]
@@ -274,16 +277,8 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, prefix_lens, extend_l
                                  ws.numel() * ws.element_size(), _stream_handle(stream)))
 
 
-def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale: float, out,
-                     lse=None, workspace=None, stream=None, timed: bool = False):
-    """Chunked-prefill extend attention over the paged cache.
-
-    q, out: device ``[sum(E), Hq, D]``; lse: device float32 ``[sum(E), Hq]`` or None;
-    prefix_lens / extend_lens: host, one entry per block_table row.
-    Returns ``out``; with ``timed`` (bf16 only) the measurement variant runs and
-    ``(out, stamps, tick_hz)`` is returned, ``stamps`` a device int64 ``[items, 4]``
-    of {start, end, kind (0 chunk, 1 decode / verify), request} per work item.
-    """
+def _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale, out, lse, workspace, stream):
+    """Checks shared by the extend-attention entry points; returns (lib, p, e, hkv, d, args)."""
     import torch
     lib = load_library()
     nb, hkv, bs, d = _check_cache(k_cache, v_cache, block_table)
@@ -308,6 +303,22 @@ def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens,
             _ptr(p), _ptr(e), len(p), hq, hkv, d, bs, float(scale), code, out.data_ptr(),
             lse.data_ptr() if lse is not None else None, ws.data_ptr(), ws.numel() * ws.element_size(),
             _stream_handle(stream))
+    return lib, p, e, hkv, d, args
+
+
+def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale: float, out,
+                     lse=None, workspace=None, stream=None, timed: bool = False):
+    """Chunked-prefill extend attention over the paged cache.
+
+    q, out: device ``[sum(E), Hq, D]``; lse: device float32 ``[sum(E), Hq]`` or None;
+    prefix_lens / extend_lens: host, one entry per block_table row.
+    Returns ``out``; with ``timed`` (bf16 only) the measurement variant runs and
+    ``(out, stamps, tick_hz)`` is returned, ``stamps`` a device int64 ``[items, 4]``
+    of {start, end, kind (0 chunk, 1 decode / verify), request} per work item.
+    """
+    import torch
+    lib, _, _, _, _, args = _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale, out,
+                                         lse, workspace, stream)
     if not timed:
         _check(lib.extattn_extend_attention(*args))
         return out
@@ -320,3 +331,18 @@ def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens,
     stamps = torch.empty((n.value, 4), dtype=torch.int64, device=q.device)
     _check(lib.extattn_extend_attention_timed(*args, stamps.data_ptr(), n.value, ctypes.byref(n), ctypes.byref(hz)))
     return out, stamps, hz.value
+
+
+def extend_attention_append(q, k_new, v_new, k_cache, v_cache, block_table, prefix_lens, extend_lens,
+                            scale: float, out, lse=None, workspace=None, stream=None):
+    """KV append fused into the extend launch: writes k_new / v_new (device
+    ``[sum(E), Hkv, D]``) into the paged cache at positions prefix + t and computes
+    the same attention as ``extend_attention``, in one attention launch. Returns ``out``."""
+    lib, p, e, hkv, d, args = _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale, out,
+                                           lse, workspace, stream)
+    total = int(e.sum())
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (total, hkv, d) or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous device [sum(E), Hkv, D] tensor of q's dtype")
+    _check(lib.extattn_extend_attention_append(args[0], k_new.data_ptr(), v_new.data_ptr(), *args[1:]))
+    return out

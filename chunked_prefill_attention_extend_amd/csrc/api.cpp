@@ -189,8 +189,8 @@ int extattn_workspace_bytes(int32_t num_seqs, const int32_t* prefix_lens, const 
   if (!bytes) return fail(EXTATTN_EINVAL, "bytes must not be null");
   int rc = check_common(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, true);
   if (rc != EXTATTN_OK) return rc;
-  Plan plan;
-  rc = build_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, plan);
+  Plan plan;  // sized with the fused append's items too, so one size serves both calls
+  rc = build_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, plan, true);
   if (rc != EXTATTN_OK) return fail(rc, "planning failed");
   *bytes = plan.bytes;
   g_error.clear();
@@ -259,7 +259,8 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                 int32_t block_size, float scale, int32_t dtype, void* out, float* lse, void* workspace,
                 size_t workspace_bytes, void* stream, bool timed, int64_t* stamps, int32_t capacity,
-                int32_t* n_items, double* tick_hz) {
+                int32_t* n_items, double* tick_hz, const void* k_new = nullptr, const void* v_new = nullptr) {
+  const bool fused = k_new != nullptr || v_new != nullptr;
   int rc = check_common(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, true);
   if (rc != EXTATTN_OK) return rc;
   rc = check_blocks(num_seqs, prefix_lens, extend_lens, max_blocks, num_blocks, block_size);
@@ -268,8 +269,9 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
     return fail(EXTATTN_EINVAL, "null device pointer");
   if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(EXTATTN_EINVAL, "scale must be finite and > 0");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(EXTATTN_EINVAL, "workspace must be 256-byte aligned");
+  if (fused && (!k_new || !v_new)) return fail(EXTATTN_EINVAL, "null k_new / v_new");
   Plan plan;
-  rc = build_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, plan);
+  rc = build_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, plan, fused);
   if (rc != EXTATTN_OK) return fail(rc, "planning failed");
   if (workspace_bytes < plan.bytes) return fail(EXTATTN_ENOSPC, "workspace too small");
   if (timed) {
@@ -322,9 +324,35 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
   a.n_items = int32_t(plan.items.size());
   a.n_tasks = int32_t(plan.tasks.size());
   a.stamps = timed ? stamps : nullptr;
+  if (fused) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache_w = const_cast<void*>(k_cache);
+    a.v_cache_w = const_cast<void*>(v_cache);
+    a.append_done = reinterpret_cast<int32_t*>(ws + kAppendDoneOffset);
+    a.n_append = plan.n_append;
+  }
 
   hipError_t e;
   if (dtype == EXTATTN_F32) {
+    if (fused) {  // fp32: the append runs as its own launch first, on the same stream
+      KvArgs ka{};
+      ka.k_new = k_new;
+      ka.v_new = v_new;
+      ka.k_cache = const_cast<void*>(k_cache);
+      ka.v_cache = const_cast<void*>(v_cache);
+      ka.block_table = block_table;
+      ka.seqs = a.seqs;
+      ka.err = a.err;
+      ka.num_blocks = num_blocks;
+      ka.max_blocks = max_blocks;
+      ka.num_seqs = num_seqs;
+      ka.hkv = num_kv_heads;
+      ka.head_dim = head_dim;
+      ka.total_tokens = int32_t(plan.total_rows);
+      e = launch_kv_append(ka, dtype, st);
+      if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+    }
     e = launch_attn_f32(a, st);
     if (e != hipSuccess) return hip_fail(e, "fp32 attention launch");
   } else {
@@ -354,6 +382,18 @@ int extattn_extend_attention(const void* q, const void* k_cache, const void* v_c
   return extend_call(q, k_cache, v_cache, block_table, max_blocks, num_blocks, prefix_lens, extend_lens, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, scale, dtype, out, lse, workspace,
                      workspace_bytes, stream, false, nullptr, 0, nullptr, nullptr);
+}
+
+int extattn_extend_attention_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                    void* v_cache, const int32_t* block_table, int32_t max_blocks,
+                                    int64_t num_blocks, const int32_t* prefix_lens, const int32_t* extend_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, float scale, int32_t dtype, void* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new) return fail(EXTATTN_EINVAL, "null k_new / v_new");
+  return extend_call(q, k_cache, v_cache, block_table, max_blocks, num_blocks, prefix_lens, extend_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, scale, dtype, out, lse, workspace,
+                     workspace_bytes, stream, false, nullptr, 0, nullptr, nullptr, k_new, v_new);
 }
 
 int extattn_extend_attention_timed(const void* q, const void* k_cache, const void* v_cache,

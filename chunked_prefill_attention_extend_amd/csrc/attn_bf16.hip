@@ -806,6 +806,73 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused append. Append items copy new tokens of one request from k_new / v_new
+// into the paged cache (K as one 16-byte store per piece, V scattered into the
+// slot-minor layout), then each wave adds 1 to the completion counter with
+// release semantics at device scope. An attention item whose key range reaches
+// the request's new keys waits, before its first load, until the counter says
+// that every append wave is done. The append items lead the launch order and
+// every die dispatches its workgroups in order, so the waits end; the wait is
+// still bounded and leaves kErrWaitTimeout in the error word if it gives up.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ void append_item(const AttnArgs& a, const WorkItem& it) {
+  constexpr int PIECES = D / 8;  // 16-byte pieces of a head vector
+  const SeqInfo si = a.seqs[it.seq];
+  const int per_tok = a.hkv * PIECES;
+  const int n = it.nrows * per_tok;
+  const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int t = i / per_tok;
+    const int rem = i - t * per_tok;
+    const int g = rem / PIECES, c = rem - g * PIECES;
+    const int tok = it.row0 + t;  // new token index within the request
+    const int pos = si.prefix + tok;
+    const int32_t phys = bt[pos / kBlockSize];
+    if (!block_ok(phys, a.num_blocks)) {
+      if (g == 0 && c == 0) atomicAdd(a.err, 1);
+      continue;
+    }
+    const int slot = pos % kBlockSize;
+    const int64_t src = (int64_t(si.q_off + tok) * a.hkv + g) * D + c * 8;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k_new) + src);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v_new) + src);
+    uint16_t* kc = static_cast<uint16_t*>(a.k_cache_w) + ((int64_t(phys) * a.hkv + g) * kBlockSize + slot) * D + c * 8;
+    *reinterpret_cast<u32x4*>(kc) = kv;
+    uint16_t* vc = static_cast<uint16_t*>(a.v_cache_w) + (int64_t(phys) * a.hkv + g) * int64_t(D) * kBlockSize +
+                   int64_t(c * 8) * kBlockSize + slot;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = vv[e];
+      vc[(2 * e) * kBlockSize] = uint16_t(w & 0xFFFFu);
+      vc[(2 * e + 1) * kBlockSize] = uint16_t(w >> 16);
+    }
+  }
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(a.append_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kWaitSpinLimit = 1 << 20;  // polls, ~0.3 us apart: ~0.3 s
+
+// One lane polls the counter (relaxed, spaced out so that hundreds of waiting
+// workgroups do not flood one address), then one acquire fence makes the appended
+// K/V visible before the workgroup's first load.
+__device__ void wait_appends(const AttnArgs& a) {
+  if (threadIdx.x == 0) {
+    const int target = a.n_append * kWaves;
+    int spins = 0;
+    while (__hip_atomic_load(a.append_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(10);
+      if (++spins == kWaitSpinLimit) {
+        atomicOr(a.err, kErrWaitTimeout);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
@@ -821,12 +888,17 @@ void attn_bf16_kernel(AttnArgs a) {
     st[2] = it.kind;
     st[3] = it.seq;
   }
-  if (it.kind == kItemChunk)
-    chunk_item<D>(a, it, smem);
-  else if (it.nrows <= kSplitRows)
-    split_item<D, 1>(a, it, smem);
-  else
-    split_item<D, 2>(a, it, smem);
+  if (it.kind == kItemAppend) {
+    append_item<D>(a, it);
+  } else {
+    if (a.n_append > 0 && it.key_end > a.seqs[it.seq].prefix) wait_appends(a);  // reads new keys
+    if (it.kind == kItemChunk)
+      chunk_item<D>(a, it, smem);
+    else if (it.nrows <= kSplitRows)
+      split_item<D, 1>(a, it, smem);
+    else
+      split_item<D, 2>(a, it, smem);
+  }
   if (a.stamps) {
     __syncthreads();
     if (threadIdx.x == 0) a.stamps[4 * int64_t(blockIdx.x) + 1] = int64_t(wall_clock64());

@@ -37,7 +37,12 @@ struct SeqInfo {
 enum : int32_t {
   kItemChunk = 0,  // kRowsPerTile rows of one (request, KV head); all waves share LDS K/V tiles
   kItemSplit = 1,  // <= kSplitMaxRows rows; each wave takes its own part of the key range
+  kItemAppend = 2, // fused append: copy new tokens [row0, row0 + nrows) of a request into the cache
 };
+
+constexpr int kAppendTokens = 16;  // tokens per append item of a fused append + attention launch
+constexpr int kAppendDoneOffset = 128;  // byte offset of the append completion counter in the workspace header
+constexpr int32_t kErrWaitTimeout = 1 << 30;  // error-word bit: an attention item stopped waiting for the appends
 
 // One workgroup's work. Rows are flattened per (request, KV head) as
 // row = pos * group + head_in_group, pos in [0, E), head_in_group in [0, group).
@@ -99,6 +104,15 @@ struct AttnArgs {
   int32_t n_items;
   int32_t n_tasks;
   int64_t* stamps;   // NULL, or [n_items][4] {start, end, kind, request} in wall-clock ticks
+  // fused append (n_append > 0): the first n_append items copy k_new / v_new
+  // [sum(E), Hkv, D] into the cache; every wave of them adds 1 to *append_done
+  // (release), and attention items that read new keys wait for n_append * kWaves
+  const void* k_new;
+  const void* v_new;
+  void* k_cache_w;
+  void* v_cache_w;
+  int32_t* append_done;
+  int32_t n_append;
 };
 
 struct KvArgs {
@@ -124,6 +138,7 @@ struct Plan {
   std::vector<CombineTask> tasks;
   int64_t n_slot_floats = 0;  // size of the partial-slot area
   int32_t split_keys = 0;  // keys per split workgroup (0: no split items)
+  int32_t n_append = 0;    // append items at the head of `items` (fused append launch)
   int64_t total_rows = 0;
   // byte offsets inside the workspace
   size_t off_zero = 0, off_seqs = 0, off_items = 0, off_tasks = 0, off_slots = 0, bytes = 0, upload_bytes = 0;
@@ -134,7 +149,7 @@ constexpr size_t kZeroPageBytes = size_t(kBlockSize) * 128 * 4;  // one (block, 
 
 // plan.cpp
 int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
-               int32_t head_dim, int32_t dtype, Plan& plan);
+               int32_t head_dim, int32_t dtype, Plan& plan, bool with_append = false);
 
 // budget.cpp
 int token_budget_step_impl(int32_t n_running, const int64_t* running_total, const int64_t* running_computed,

@@ -138,13 +138,14 @@ static void order_items(std::vector<std::vector<WorkItem>>& groups, std::vector<
 // merges the workgroups' partials. Longer chunks take the chunk path:
 // kRowsPerTile-row tiles over their whole causal key range.
 int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
-               int32_t head_dim, int32_t dtype, Plan& plan) {
+               int32_t head_dim, int32_t dtype, Plan& plan, bool with_append) {
   const int32_t group = hq / hkv;
   plan.seqs.resize(num_seqs);
   plan.items.clear();
   plan.tasks.clear();
   plan.n_slot_floats = 0;
   plan.split_keys = 0;
+  plan.n_append = 0;
   int64_t q_off = 0;
   for (int32_t r = 0; r < num_seqs; ++r) {
     plan.seqs[r] = SeqInfo{static_cast<int32_t>(q_off), prefix[r], extend[r], 0};
@@ -249,6 +250,17 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
       }
     }
     order_items(groups, split_items, plan.items);
+    if (with_append) {
+      // Fused append: the copies of the new tokens come first in the launch, so
+      // every die dispatches them before any attention item that waits for them.
+      std::vector<WorkItem> app;
+      for (int32_t r = 0; r < num_seqs; ++r)
+        for (int32_t t = 0; t < extend[r]; t += kAppendTokens)
+          app.push_back(WorkItem{kItemAppend, r, 0, t, std::min(kAppendTokens, extend[r] - t), 0, 0, -1, -1,
+                                 {0, 0, 0}});
+      plan.n_append = int32_t(app.size());
+      plan.items.insert(plan.items.begin(), app.begin(), app.end());
+    }
   }
 
   size_t off = kHeaderBytes;

@@ -236,6 +236,34 @@ int extattn_extend_attention(const void* q, const void* k_cache, const void* v_c
                              void* stream);
 
 /*
+ * KV append fused into the extend launch: the same result as
+ * extattn_kv_append(k_new, v_new, ...) followed by extattn_extend_attention(...)
+ * on the same requests, in one attention launch. The chunk's own keys and
+ * values are the part of the extend equation computed in this round (zdszero
+ * notes, section "prefill as several resumable extends"); here the launch's
+ * first workgroups write them into the paged cache and the attention
+ * workgroups that reach a request's new keys wait until those writes are done
+ * (a device-scope counter in the workspace, release / acquire; the wait is
+ * bounded: if it gives up, bit 30 of the error word is set and the results are
+ * not valid). Prefix keys need no wait.
+ *
+ * k_new, v_new: device [sum(E), Hkv, D], element type of q, request order;
+ *               token q_off_r + t of request r goes to position prefix_lens[r] + t.
+ * k_cache, v_cache: written (the new tokens' slots) and read.
+ * Other arguments, ownership and errors as for extattn_extend_attention; the
+ * workspace size is the same extattn_workspace_bytes() result. Block ids
+ * outside [0, num_blocks) are skipped for writing and read as zeros, and
+ * counted in the error word. fp32 runs the append as its own launch first on
+ * the same stream.
+ */
+int extattn_extend_attention_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                    void* v_cache, const int32_t* block_table, int32_t max_blocks,
+                                    int64_t num_blocks, const int32_t* prefix_lens, const int32_t* extend_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, float scale, int32_t dtype, void* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Measurement variant of extattn_extend_attention: the same work and the same
  * results, and each workgroup of the bf16 attention kernel (one work item: a
  * chunk tile, a piece of one, or a piece of a decode / verify request's key

@@ -1,0 +1,84 @@
+"""KV append fused into the extend launch (needs a gfx950 GPU).
+
+``extend_attention_append`` must leave the paged cache bit for bit as
+``kv_append`` does and give the same ``out`` / ``lse`` bit for bit as
+``kv_append`` followed by ``extend_attention`` (the attention work items are
+the same; only where the new tokens' K/V come from in time differs), with no
+error word set. One case is also compared with the oracle directly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunked_prefill_attention_extend_amd as ext
+from synth import custom_workload
+from tests.harness import PagedCache, check_launch, dev_tensor, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+def _run_both(w):
+    reqs = w.requests
+    prefix = [r.launch[0] for r in reqs]
+    extend = [r.launch[1] for r in reqs]
+    idx = [r.index for r in reqs]
+    q = np.concatenate([w.q(r, p, p + e) for r, p, e in zip(reqs, prefix, extend)])
+    k_new = np.concatenate([w.k(r, p, p + e) for r, p, e in zip(reqs, prefix, extend)])
+    v_new = np.concatenate([w.v(r, p, p + e) for r, p, e in zip(reqs, prefix, extend)])
+    qd, kd, vd = dev_tensor(q, w.dtype), dev_tensor(k_new, w.dtype), dev_tensor(v_new, w.dtype)
+    # separate: every token appended by kv_append, then attention
+    sep = PagedCache(w)
+    for r in reqs:
+        p, e = r.launch
+        sep.append([r.index], [0], w.k(r, 0, p + e), w.v(r, 0, p + e), [p + e])
+    o1, l1 = sep.attend(idx, prefix, extend, q)
+    # fused: prefixes appended beforehand, the new tokens by the attention launch
+    fus = PagedCache(w)
+    for r in reqs:
+        p, _ = r.launch
+        if p:
+            fus.append([r.index], [0], w.k(r, 0, p), w.v(r, 0, p), [p])
+    o2 = torch.empty_like(qd)
+    l2 = torch.empty((qd.shape[0], w.n_q_heads), dtype=torch.float32, device="cuda")
+    hkv, d = w.n_kv_heads, w.head_dim
+    code = ext.EXTATTN_BF16 if w.dtype == "bf16" else ext.EXTATTN_F32
+    ws = torch.zeros(ext.workspace_bytes(prefix, extend, w.n_q_heads, hkv, d, code), dtype=torch.uint8,
+                     device="cuda")
+    ext.extend_attention_append(qd, kd, vd, fus.k, fus.v, fus.bt, prefix, extend, w.scale, o2, l2, workspace=ws)
+    torch.cuda.synchronize()
+    err = int(ws[:4].view(torch.int32).item())
+    return (o1, l1, sep), (o2, l2, fus), err, q
+
+
+@pytest.mark.parametrize("case", [
+    # (launches, Hq, Hkv, D, dtype)
+    ([(3000, 1), (900, 600), (4000, 5), (12, 1), (0, 300)], 32, 8, 128, "bf16"),  # decode, verify, chunk, P=0
+    ([(5000, 1024)], 64, 8, 128, "bf16"),   # one sweep-like chunk, prefix ending inside a block
+    ([(6000, 700)], 32, 8, 128, "bf16"),    # chunk tiles cut into key pieces (pure-prefix pieces do not wait)
+    ([(777, 40), (33, 1), (0, 17)], 16, 2, 64, "bf16"),  # D=64
+    ([(50, 30), (129, 1)], 8, 2, 128, "f32"),  # fp32: append launch, then attention
+])
+def test_fused_append_matches_separate(case):
+    launches, hq, hkv, d, dt = case
+    w = custom_workload(700 + len(launches) + hq + d, launches, hq, hkv, d, dtype=dt,
+                        mult=0.5 if dt == "bf16" else 1.0)
+    log(f"fused append {launches} Hq={hq} Hkv={hkv} D={d} {dt}")
+    (o1, l1, sep), (o2, l2, fus), err, q = _run_both(w)
+    assert err == 0, f"error word {err:#x}"
+    assert torch.equal(_bits(sep.k), _bits(fus.k)), "K cache differs from kv_append's"
+    assert torch.equal(_bits(sep.v), _bits(fus.v)), "V cache differs from kv_append's"
+    assert torch.equal(o1, o2), "out differs from append + extend"
+    assert torch.equal(l1, l2), "lse differs from append + extend"
+
+
+def test_fused_append_against_oracle():
+    w = custom_workload(777, [(2000, 1), (1500, 400), (0, 64)], 32, 8, 128)
+    log("fused append against the oracle")
+    _, (o2, l2, _), err, q = _run_both(w)
+    assert err == 0
+    offs = np.concatenate([[0], np.cumsum([r.launch[1] for r in w.requests])[:-1]]).astype(int)
+    check_launch(w, o2, l2, {r.index: int(o) for r, o in zip(w.requests, offs)}, q, what="fused append")
