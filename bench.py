@@ -157,10 +157,10 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
 
     def timed(fn):
         """GPU time of one call (its metadata copy and kernels), median over reps. The
-        GPU is first given a few ms of fills so that the host enqueues every call ahead
+        GPU is first given ~10 ms of fills so that the host enqueues every call ahead
         of the GPU: the events then bracket device work only, not host-side planning."""
         torch.cuda.synchronize()
-        for _ in range(20):
+        for _ in range(100):
             flush.fill_(0x5A)
         evs = []
         for i in range(reps + 2):
@@ -252,7 +252,7 @@ def verify_rows_sweep(torch, ext, synth, reps: int = 10):
         ws = torch.empty(ext.workspace_bytes(prefix, extend, hq, hkv, d, ext.EXTATTN_BF16), dtype=torch.uint8,
                          device=dev)
         torch.cuda.synchronize()
-        for _ in range(20):
+        for _ in range(100):
             flush.fill_(0x5A)
         evs = []
         for i in range(reps + 2):
@@ -396,6 +396,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--only-mixed", action="store_true", help="run only the mixed-step measurement (for profiling)")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused append + attention steps")
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="only measure attention TFLOP/s against the chunk size (one 64k prompt)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -465,17 +466,19 @@ def main() -> int:
     value = flops / (dt / args.steps) / 1e12
 
     # The same steps with each chunk's append fused into its attention launch.
-    for i in range(args.warmup):
-        sweep_step(ext, s, fused=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        sweep_step(ext, s, fused=True)
-    torch.cuda.synchronize()
-    dtf = time.perf_counter() - t0
-    fused = {"ms_per_step": dtf / args.steps * 1e3, "tflops": flops / (dtf / args.steps) / 1e12,
-             "note": "128 x extend_attention_append (append inside the attention launch)"}
-    log(f"fused steps: {dtf / args.steps * 1e3:.1f} ms per step")
+    fused = None
+    if not args.no_fused:
+        for i in range(args.warmup):
+            sweep_step(ext, s, fused=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            sweep_step(ext, s, fused=True)
+        torch.cuda.synchronize()
+        dtf = time.perf_counter() - t0
+        fused = {"ms_per_step": dtf / args.steps * 1e3, "tflops": flops / (dtf / args.steps) / 1e12,
+                 "note": "128 x extend_attention_append (append inside the attention launch)"}
+        log(f"fused steps: {dtf / args.steps * 1e3:.1f} ms per step")
 
     mixed = None
     if not args.no_mixed:

@@ -297,8 +297,12 @@ def _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, sca
                             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [sum(E), Hq] tensor")
     code = _dtype_code(q)
-    need = workspace_bytes(p, e, hq, hkv, d, code)
-    ws = _workspace(need, q.device, workspace)
+    if workspace is None:
+        ws = _workspace(workspace_bytes(p, e, hq, hkv, d, code), q.device, None)
+    else:  # the library checks the size itself (EXTATTN_ENOSPC): no second planning pass here
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or not workspace.is_cuda:
+            raise ValueError("workspace must be a contiguous uint8 device tensor")
+        ws = workspace
     args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1], nb,
             _ptr(p), _ptr(e), len(p), hq, hkv, d, bs, float(scale), code, out.data_ptr(),
             lse.data_ptr() if lse is not None else None, ws.data_ptr(), ws.numel() * ws.element_size(),
