@@ -82,3 +82,32 @@ def test_fused_append_against_oracle():
     assert err == 0
     offs = np.concatenate([[0], np.cumsum([r.launch[1] for r in w.requests])[:-1]]).astype(int)
     check_launch(w, o2, l2, {r.index: int(o) for r, o in zip(w.requests, offs)}, q, what="fused append")
+
+
+def test_fused_append_invalid_block_ids_are_counted_not_written():
+    """A new token whose block id is out of range is neither written nor read
+    (the zero page stands in) and is counted in the error word; the other
+    blocks are written as kv_append writes them."""
+    w = custom_workload(781, [(40, 24)], 8, 8, 128)
+    r = w.requests[0]
+    fus = PagedCache(w, fill=0.0)
+    fus.append([0], [0], w.k(r, 0, 40), w.v(r, 0, 40), [40])
+    bad = fus.bt.clone()
+    bad[0, 3] = w.num_blocks + 1000      # block of positions 48..63 (new tokens 8..23)
+    q = dev_tensor(w.q(r, 40, 64), w.dtype)
+    kn = dev_tensor(w.k(r, 40, 64), w.dtype)
+    vn = dev_tensor(w.v(r, 40, 64), w.dtype)
+    out = torch.empty_like(q)
+    ws = torch.zeros(ext.workspace_bytes([40], [24], 8, 8, 128, ext.EXTATTN_BF16), dtype=torch.uint8,
+                     device="cuda")
+    before = fus.k.clone()
+    ext.extend_attention_append(q, kn, vn, fus.k, fus.v, bad, [40], [24], w.scale, out, None, workspace=ws)
+    torch.cuda.synchronize()
+    err = int(ws[:4].view(torch.int32).item())
+    assert err > 0 and not (err & (1 << 30)), f"error word {err:#x}"
+    assert torch.isfinite(out.float()).all()
+    blocks = [int(b) for b in r.blocks]
+    # positions 40..47 (block 2) were written; nothing else changed
+    assert not torch.equal(fus.k[blocks[2]], before[blocks[2]])
+    others = [b for b in range(w.num_blocks) if b != blocks[2]]
+    assert torch.equal(fus.k[others], before[others])

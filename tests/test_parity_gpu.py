@@ -57,6 +57,7 @@ def test_sweep128k_sampled_chunks():
     ([(1000, 3), (5, 4)], 32, 4, 128),    # verify rows of 24 and 32 rows (split path, two row blocks)
     ([(500, 2), (64, 3), (2047, 4)], 32, 8, 128),  # verify rows of 8, 12, 16 rows (split path, one row block)
     ([(777, 2)], 64, 8, 64),              # 16 split rows at two positions, D=64
+    ([(500, 3), (31, 4)], 64, 8, 64),     # 24 and 32 split rows (two row blocks), D=64
     ([(77, 5)], 64, 8, 128),              # 40 rows: one partial chunk tile
     ([(3000, 9), (40, 8)], 64, 8, 64),    # 72 and 64 rows: partial chunk tiles, D=64
     ([(300, 17)], 64, 1, 128),            # one KV head for 64 query heads
