@@ -271,7 +271,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   // Each wave copies one 1 KB piece of every K and V tile (waves beyond the piece
   // count copy nothing); piece `wave` lies in block my_blk of the tile.
   static_assert(NINST == 1, "one piece per wave and tile");
-  const bool has_piece = wave < PIECES;
+  const bool has_piece = PIECES >= kWaves || wave < PIECES;  // compile-time true when every wave has one
   const int my_blk = has_piece ? wave / (PIECES / 2) : 0;
   // The ids of a 32-tile window (64 entries) sit one per lane in `idwin`, loaded from
   // the ring once per window and checked there: entries past the sequence end and
@@ -292,10 +292,6 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     const int32_t v = __builtin_amdgcn_readlane(idwin, ((j - t0) & 31) * 2 + my_blk);
     return j < t1 ? v : -1;
   };
-  auto block_base = [&](const uint16_t* cache, int32_t blk) -> const unsigned char* {
-    return blk < 0 ? static_cast<const unsigned char*>(a.zero_page)
-                   : reinterpret_cast<const unsigned char*>(cache + (int64_t(blk) * a.hkv + g) * (kBlockSize * D));
-  };
   // Per-lane byte offsets (within the piece's block) of this wave's direct loads.
   uint32_t k_src[NINST], v_src[NINST];
 #pragma unroll
@@ -309,11 +305,22 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     const int d = ((i * 64 + lane) % (VSUB / 16)) / 2, cv = lane & 1;
     v_src[x] = uint32_t((d * kBlockSize + ((cv ^ swz_v(d)) * 8)) * 2);
   }
+  // Copy sources and destinations as scalars computed once: this (request, KV head)'s
+  // first block in each cache, the byte stride between blocks, and this wave's LDS
+  // piece in K slot 0 / V slot 0 (slots are KT_BYTES apart).
+  const unsigned char* kc_g = reinterpret_cast<const unsigned char*>(kc + int64_t(g) * (kBlockSize * D));
+  const unsigned char* vc_g = reinterpret_cast<const unsigned char*>(vc + int64_t(g) * (kBlockSize * D));
+  const uint64_t blk_bytes = uint64_t(a.hkv) * (kBlockSize * D * 2);
+  const uint32_t k_dst = lds_addr(smem + KBUF) + wave * 1024;
+  const uint32_t v_dst = lds_addr(smem + VBUF) + wave * 1024;
+  auto src_base = [&](const unsigned char* cache_g, int32_t blk) -> const unsigned char* {
+    return blk < 0 ? static_cast<const unsigned char*>(a.zero_page) : cache_g + uint64_t(uint32_t(blk)) * blk_bytes;
+  };
   auto issue_k = [&](int32_t blk, int slot) {
-    if (has_piece) dma16(block_base(kc, blk), k_src[0], lds_addr(smem + KBUF + slot * KT_BYTES + wave * 1024));
+    if (has_piece) dma16(src_base(kc_g, blk), k_src[0], k_dst + slot * KT_BYTES);
   };
   auto issue_v = [&](int32_t blk, int slot) {
-    if (has_piece) dma16(block_base(vc, blk), v_src[0], lds_addr(smem + VBUF + slot * KT_BYTES + wave * 1024));
+    if (has_piece) dma16(src_base(vc_g, blk), v_src[0], v_dst + slot * KT_BYTES);
   };
 
   f32x16 o[DB];
