@@ -284,13 +284,14 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     const bool ok = block_ok(v, a.num_blocks);
     const uint64_t bad = __builtin_amdgcn_ballot_w64(inside && !ok);
     if (bad != 0 && wave == 0 && lane == 0) atomicAdd(a.err, int(__builtin_popcountll(bad)));
-    idwin = (inside && ok) ? v : -1;
+    // tiles past the range (padding steps) read the zero page even where the
+    // sequence still has keys
+    const bool in_range = t0 + 32 * k + (lane >> 1) < t1;
+    idwin = (inside && ok && in_range) ? v : -1;
   };
-  // This wave's block id of tile j (wave-uniform); tiles past the range (padding
-  // steps) read the zero page even where the sequence still has keys.
+  // This wave's block id of tile j (wave-uniform).
   auto read_blk = [&](int j) -> int32_t {
-    const int32_t v = __builtin_amdgcn_readlane(idwin, ((j - t0) & 31) * 2 + my_blk);
-    return j < t1 ? v : -1;
+    return __builtin_amdgcn_readlane(idwin, ((j - t0) & 31) * 2 + my_blk);
   };
   // Per-lane byte offsets (within the piece's block) of this wave's direct loads.
   uint32_t k_src[NINST], v_src[NINST];
@@ -310,11 +311,12 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   // piece in K slot 0 / V slot 0 (slots are KT_BYTES apart).
   const unsigned char* kc_g = reinterpret_cast<const unsigned char*>(kc + int64_t(g) * (kBlockSize * D));
   const unsigned char* vc_g = reinterpret_cast<const unsigned char*>(vc + int64_t(g) * (kBlockSize * D));
-  const uint64_t blk_bytes = uint64_t(a.hkv) * (kBlockSize * D * 2);
+  const uint32_t blk_bytes = uint32_t(a.hkv) * (kBlockSize * D * 2);  // < 2^32: 32x32 -> 64-bit product below
   const uint32_t k_dst = lds_addr(smem + KBUF) + wave * 1024;
   const uint32_t v_dst = lds_addr(smem + VBUF) + wave * 1024;
   auto src_base = [&](const unsigned char* cache_g, int32_t blk) -> const unsigned char* {
-    return blk < 0 ? static_cast<const unsigned char*>(a.zero_page) : cache_g + uint64_t(uint32_t(blk)) * blk_bytes;
+    const unsigned char* p = cache_g + uint64_t(uint32_t(max(blk, 0))) * uint64_t(blk_bytes);
+    return blk < 0 ? static_cast<const unsigned char*>(a.zero_page) : p;
   };
   auto issue_k = [&](int32_t blk, int slot) {
     if (has_piece) dma16(src_base(kc_g, blk), k_src[0], k_dst + slot * KT_BYTES);
@@ -351,9 +353,11 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   };
   // Causal mask of a diagonal tile (and of keys past the range end). Element i holds
   // key kt + 8 hi + key_of_elem(i, 0), so the test is one threshold against constants.
+  // first tile index whose last key passes lim_min (tiles from there on may need masking)
+  const int j_mask = lim_min >= KT - 1 ? (lim_min - (KT - 1)) / KT + 1 : 0;
   auto mask = [&](int j, f32x16& s) {
     const int kt = j * KT;
-    if (kt + KT - 1 > lim_min) {
+    if (j >= j_mask) {
       const int t = lim - kt - 8 * hi;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -423,6 +427,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   // can reach past the end; its V tile is cleared in LDS once, after it has landed
   // and before it is read (the caller puts barriers around this).
   const bool tail_clip = (t1 * KT > kv_len);
+  const int j_clip = tail_clip ? t1 - 2 : INT_MIN;  // step whose next tile is the clipped last one
   auto clip_tail = [&](int slot) {
     unsigned char* base = smem + VBUF + slot * KT_BYTES;
     const int kt = (t1 - 1) * KT;
@@ -483,9 +488,14 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       constexpr int sl = decltype(slot_tag)::value;  // u % 4
       const int j = t0 + u;
       // ids of tiles j+32 .. j+63 replace those of tiles j-32 .. j-1 (long consumed);
-      // the first read (tile j+32, by step u+29) comes after two barriers
-      if ((u & 31) == 0 && u > 0) fill_ids(j + 32);
-      if (((u + 3) & 31) == 0) load_window((u + 3) >> 5);  // tile j+3 starts a new window
+      // the first read (tile j+32, by step u+29) comes after two barriers. u = sl (mod 4),
+      // so only step 0 can start a 32-step period and only step 1 a new window.
+      if constexpr (sl == 0) {
+        if ((u & 31) == 0 && u > 0) fill_ids(j + 32);
+      }
+      if constexpr (sl == 1) {
+        if (((u + 3) & 31) == 0) load_window((u + 3) >> 5);  // tile j+3 starts a new window
+      }
       const int32_t bk = read_blk(j + 3);
       issue_k(bk, (sl + 3) & 3);
       issue_v(pending, (sl + 2) & 3);
@@ -536,7 +546,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       __builtin_amdgcn_sched_barrier(0);
       mask(j + 1, snext);
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(kIssuePerStep) : "memory");
-      if (tail_clip && j + 1 == t1 - 1) {  // V(j+1) has landed: clear its keys past the end
+      if (j == j_clip) {  // V(j+1) has landed: clear its keys past the end
         clip_tail((sl + 1) & 3);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
