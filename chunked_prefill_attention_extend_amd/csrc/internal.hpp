@@ -18,7 +18,7 @@ constexpr int kChunkKeys = 32;    // chunk path: keys per LDS K/V tile (one 32x3
 constexpr int kSplitTile = 32;    // split path: keys per register K/V tile
 constexpr int kSplitKeysMin = 1024;  // split path: keys per workgroup (kWaves waves), lower bound
 constexpr int kSplitKeysMax = 8192;  // upper bound: a wave's block ids fit one per lane
-constexpr int kSplitTargetItems = 512;  // split path aims at this many workgroups (2 per CU on 256 CUs)
+constexpr int kSplitTargetItems = 256;  // split path aims at this many workgroups (1 per CU on 256 CUs)
 constexpr int kChunkTargetItems = 256;  // chunk rows: split key ranges until about this many workgroups (1 per CU)
 constexpr int kChunkMinPieceKeys = 2048;  // ... with at least this many keys per piece
 constexpr int kCombineRows = 32;         // rows per combine task of split chunk tiles
