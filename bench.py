@@ -178,6 +178,14 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
                                                workspace=ws))
     (t_dec, t_dec_min) = timed(lambda: ext.extend_attention(q_dec, k_cache, v_cache, bt_dec, [prefix[i] for i in dec],
                                                [1] * len(dec), w.scale, out_dec, lse_dec, workspace=ws))
+    ci = [i for i in range(len(reqs)) if i not in dec]
+    c_off = sum(extend[i] for i in dec)   # the chunk's rows follow the decode rows
+    q_chk = q[c_off:]
+    out_chk = torch.empty_like(q_chk)
+    lse_chk = torch.empty((q_chk.shape[0], hq), dtype=torch.float32, device=dev)
+    bt_chk = torch.from_numpy(bt_all[ci]).to(dev)
+    (t_chk, t_chk_min) = timed(lambda: ext.extend_attention(q_chk, k_cache, v_cache, bt_chk, [prefix[i] for i in ci],
+                                               [extend[i] for i in ci], w.scale, out_chk, lse_chk, workspace=ws))
     dec_bytes = 0
     for i in dec:
         L = prefix[i] + 1
@@ -215,6 +223,8 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
         "attention_kernel_span_ms": kspan * 1e3,
         "span_note": "per-workgroup wall-clock stamps (measurement variant of the same launch), median of %d" % reps,
         "chunk_flops": chunk_flops,
+        "ms_chunk_rows_only": t_chk * 1e3,
+        "chunk_tflops_alone": chunk_flops / t_chk / 1e12,
         "mixed_lower_bound_ms": max(chunk_flops / (PEAK_BF16_TFLOPS * 1e12), dec_bytes / (PEAK_HBM_GBS * 1e9)) * 1e3,
     }
 
@@ -355,6 +365,103 @@ def chunk_size_sweep(torch, ext, synth, n: int = 65536, sizes=(256, 512, 1024, 2
             "flops": sweep_flops(ext.chunk_plan(n, sizes[0], 0.0)["chunks"], hq, d), "rows": rows}
 
 
+def config_table(torch, ext, synth, reps: int = 5):
+    """GPU time of the pages' single-prompt workloads (tiny fp32 64 tokens at C=16;
+    a 4000-token prompt at C=512; 32768 tokens at hit rate 0.5 and C=8192): each
+    planned chunk's K/V is appended, then its extend launch is timed with HIP
+    events (median of reps). The mixed step and the 128k sweep are the default
+    bench lines."""
+    out = []
+    for name in ("tiny_f32", "prompt4000", "prefix_cache32k"):
+        w = synth.make_workload(name)
+        n, c, h = w.plan
+        plan = ext.chunk_plan(n, c, h)
+        hq, hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
+        dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        mult = w.mult
+        q = synth.device_normal((n, hq, d), 8001, mult, dt)
+        kn = synth.device_normal((n, hkv, d), 8002, mult, dt)
+        vn = synth.device_normal((n, hkv, d), 8003, mult, dt)
+        k_cache = torch.zeros((w.num_blocks, hkv, 16, d), dtype=dt, device="cuda")
+        v_cache = torch.zeros((w.num_blocks, hkv, d, 16), dtype=dt, device="cuda")
+        bt = torch.from_numpy(w.block_table()).cuda()
+        out_t = torch.empty_like(q)
+        lse = torch.empty((n, hq), dtype=torch.float32, device="cuda")
+        cached = plan["cached"]
+        if cached:
+            ext.kv_append(kn[:cached], vn[:cached], k_cache, v_cache, bt, [0], [cached])
+        chunks = []
+        for p_, e_ in plan["chunks"]:
+            ext.kv_append(kn[p_:p_ + e_], vn[p_:p_ + e_], k_cache, v_cache, bt, [p_], [e_])
+            ts = []
+            for _ in range(reps + 1):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                ext.extend_attention(q[p_:p_ + e_], k_cache, v_cache, bt, [p_], [e_], w.scale, out_t[p_:p_ + e_],
+                                     lse[p_:p_ + e_])
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e-3)
+            t = float(np.median(ts[1:]))
+            f = sweep_flops([(p_, e_)], hq, d)
+            chunks.append({"prefix": p_, "extend": e_, "ms": t * 1e3, "tflops": f / t / 1e12})
+        tot_f = sum(sweep_flops([(x["prefix"], x["extend"])], hq, d) for x in chunks)
+        tot_t = sum(x["ms"] for x in chunks) * 1e-3
+        out.append({"workload": name, "dtype": w.dtype, "chunks": chunks, "flops": tot_f,
+                    "attention_ms": tot_t * 1e3, "tflops": tot_f / tot_t / 1e12})
+        log(f"{name}: {len(chunks)} chunks, {tot_t * 1e3:.3f} ms, {tot_f / tot_t / 1e12:.1f} TFLOP/s")
+    return out
+
+
+def _oracle_rate(w, rows, n_rows: int, rng):
+    """Time the CPU oracle on n_rows random rows of ``rows`` ((request, position)
+    pairs, all query heads each), called once per request with all of that
+    request's sampled rows (its intended use). Inputs are generated before timing.
+    Returns (flops timed, seconds, rows timed)."""
+    import oracle
+    sample = [rows[i] for i in rng.permutation(len(rows))[:n_rows]]
+    by_req = {}
+    for ri, pos in sample:
+        by_req.setdefault(ri, []).append(pos)
+    args = []
+    for ri, ps in by_req.items():
+        req = w.requests[ri]
+        m = max(ps) + 1
+        q = np.concatenate([w.q(req, p_, p_ + 1) for p_ in ps])
+        args.append((q, w.k(req, 0, m), w.v(req, 0, m), ps))
+    t0 = time.perf_counter()
+    for q, kk, vv, ps in args:
+        oracle.attend_rows(q, kk, vv, ps, w.scale)
+    dt = time.perf_counter() - t0
+    f = sum(4 * w.head_dim * w.n_q_heads * (p_ + 1) for _, p_ in sample)
+    return f, dt, len(sample)
+
+
+def config_oracle_times(n_rows: int = 64):
+    """The CPU oracle on each of the pages' five workloads (a timed random sample of
+    the rows their launches compute, all heads): its rate, and its wall time for
+    the whole workload extrapolated from that rate."""
+    import oracle
+    import synth
+    rng = np.random.default_rng(1)
+    res = []
+    for name in ("tiny_f32", "prompt4000", "prefix_cache32k", "mixed_budget2048", "sweep128k"):
+        w = synth.make_workload(name)
+        if w.plan is not None:
+            n, c, h = w.plan
+            launches = [(0, p_, e_) for p_, e_ in oracle.chunk_plan(n, c, h)["chunks"]]
+        else:
+            launches = [(r.index, r.launch[0], r.launch[1]) for r in w.requests]
+        total_f = sum(4 * w.head_dim * w.n_q_heads * (e_ * p_ + e_ * (e_ + 1) // 2) for _, p_, e_ in launches)
+        rows = [(ri, p_ + i) for ri, p_, e_ in launches for i in range(e_)]
+        f, dt, k = _oracle_rate(w, rows, n_rows, rng)
+        rate = f / dt
+        res.append({"workload": name, "rows_timed": k, "rows_total": len(rows), "oracle_gflops": rate / 1e9,
+                    "seconds_timed": dt, "full_seconds_estimated": total_f / rate, "full": k == len(rows)})
+        log(f"oracle {name}: {k}/{len(rows)} rows in {dt:.1f} s, {rate / 1e9:.2f} GFLOP/s")
+    return res
+
+
 def cpu_baseline(target_s: float = 15.0):
     """Time the CPU oracle on sampled rows of the sweep (chunk 64, P = 65536)."""
     import oracle
@@ -370,22 +477,23 @@ def cpu_baseline(target_s: float = 15.0):
     kk = w.k(req, 0, p0 + 1024)
     vv = w.v(req, 0, p0 + 1024)
     rng = np.random.default_rng(0)
-    rows = rng.permutation(1024)
+    rows = p0 + rng.permutation(1024)
+    qs = w.q(req, p0, p0 + 1024)
     flops = 0
     done = 0
+    block = 16  # rows per oracle call (the oracle attends any set of rows in one call)
     t0 = time.perf_counter()
-    for r in rows:
-        pos = p0 + int(r)
-        q = w.q(req, pos, pos + 1)
-        oracle.attend_rows(q, kk, vv, [pos], w.scale)
-        flops += 4 * w.head_dim * w.n_q_heads * (pos + 1)
-        done += 1
+    for b in range(0, len(rows), block):
+        pos = rows[b:b + block]
+        oracle.attend_rows(qs[pos - p0], kk, vv, pos, w.scale)
+        flops += sum(4 * w.head_dim * w.n_q_heads * (int(p_) + 1) for p_ in pos)
+        done += len(pos)
         if time.perf_counter() - t0 > target_s:
             break
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} query rows (all 64 heads) of sweep chunk 64 (P=65536), fp64 NumPy, "
-                      f"{dt:.1f} s; affinity {len(os.sched_getaffinity(0))} cpus"}
+            "sample": f"{done} query rows (all 64 heads) of sweep chunk 64 (P=65536), {block} rows per oracle "
+                      f"call, fp64 NumPy, {dt:.1f} s; affinity {len(os.sched_getaffinity(0))} cpus"}
 
 
 def main() -> int:
@@ -397,6 +505,8 @@ def main() -> int:
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--only-mixed", action="store_true", help="run only the mixed-step measurement (for profiling)")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused append + attention steps")
+    ap.add_argument("--config-table", action="store_true",
+                    help="only time the pages' smaller workloads on the GPU and the oracle on all five")
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="only measure attention TFLOP/s against the chunk size (one 64k prompt)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -428,6 +538,11 @@ def main() -> int:
         return 0
     if args.chunk_sweep:
         print(json.dumps({"chunk_size_sweep": chunk_size_sweep(torch, ext, synth)}), flush=True)
+        return 0
+    if args.config_table:
+        table = {"gpu": config_table(torch, ext, synth),
+                 "oracle": None if args.no_cpu_baseline else config_oracle_times()}
+        print(json.dumps({"config_table": table}), flush=True)
         return 0
     if args.verify_sweep:
         print(json.dumps({"verify_rows": verify_rows_sweep(torch, ext, synth)}), flush=True)
