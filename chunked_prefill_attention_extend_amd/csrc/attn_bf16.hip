@@ -227,6 +227,10 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   const int kv_len = si.prefix + si.extend;
   const int rloc = wave * kRowsPerWave + l32;
   const bool valid = rloc < it.nrows;
+  // Waves whose 32 rows all lie past the item's rows (items of few rows: verify rows,
+  // ragged last tiles) still copy their share of every K/V tile and keep the
+  // barriers, but skip the products and the softmax work (wave-uniform test).
+  const bool wave_rows = wave * kRowsPerWave < it.nrows;
   const int rho = it.row0 + rloc;
   const int pos = valid ? rho / G : 0;
   const int hh = valid ? rho - pos * G : 0;
@@ -469,14 +473,14 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     u32x4 pf[2];
     float ls;
     // The first tile sets m to the rows' exact max (0 for rows with no visible key).
-    qk(std::integral_constant<int, 0>{}, sa);
-    mask(t0, sa);
-    {
+    if (wave_rows) {
+      qk(std::integral_constant<int, 0>{}, sa);
+      mask(t0, sa);
       float mx = row_max(sa) * c2;
       mx = fmaxf(mx, partner(mx, hi));
       m = (mx == -INFINITY) ? 0.f : mx;
+      shift(sa);
     }
-    shift(sa);
     // Steady step u (tile j = t0 + u, not the last): S(j) is in scur (masked), K(j+1)
     // in K slot (u+1)%4, V(j) in V slot u%4. Issue K(j+3) and V(j+2) (their slots
     // were last read two steps ago); then
@@ -500,51 +504,53 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       issue_k(bk, (sl + 3) & 3);
       issue_v(pending, (sl + 2) & 3);
       pending = bk;
-      __builtin_amdgcn_sched_barrier(0);  // regions A and B are scheduled separately
-      // region A: the K operand reads run 3 ahead of their MFMAs, and each MFMA has
-      // one pair of tile j's weights next to it (fences keep that order)
-      {
-        constexpr int sl1 = (sl + 1) & 3;
-        const unsigned char* kb = smem + KBUF + sl1 * KT_BYTES;
-        constexpr int NPAIR = 8;  // weight pairs per lane and tile
-        static_assert(NPAIR % KS == 0 || KS % NPAIR == 0, "pairs must spread evenly over the k-steps");
-        float l0 = 0.f, l1 = 0.f;
-        u32x4 kf[KS];
+      if (wave_rows) {
+        __builtin_amdgcn_sched_barrier(0);  // regions A and B are scheduled separately
+        // region A: the K operand reads run 3 ahead of their MFMAs, and each MFMA has
+        // one pair of tile j's weights next to it (fences keep that order)
+        {
+          constexpr int sl1 = (sl + 1) & 3;
+          const unsigned char* kb = smem + KBUF + sl1 * KT_BYTES;
+          constexpr int NPAIR = 8;  // weight pairs per lane and tile
+          static_assert(NPAIR % KS == 0 || KS % NPAIR == 0, "pairs must spread evenly over the k-steps");
+          float l0 = 0.f, l1 = 0.f;
+          u32x4 kf[KS];
 #pragma unroll
-        for (int ks = 0; ks < 3 && ks < KS; ++ks) kf[ks] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ (ks << 5)));
-        snext = f32x16{};
+          for (int ks = 0; ks < 3 && ks < KS; ++ks) kf[ks] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ (ks << 5)));
+          snext = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (ks + 3 < KS) kf[ks + 3] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ ((ks + 3) << 5)));
-          snext = mfma32(kf[ks], qf[ks], snext);
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 3 < KS) kf[ks + 3] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ ((ks + 3) << 5)));
+            snext = mfma32(kf[ks], qf[ks], snext);
 #pragma unroll
-          for (int pp = ks * NPAIR / KS; pp < (ks + 1) * NPAIR / KS; ++pp) {
-            const int v = pp >> 2, w = pp & 3;
-            const float p0 = __builtin_amdgcn_exp2f(scur[8 * v + 2 * w]);
-            const float p1 = __builtin_amdgcn_exp2f(scur[8 * v + 2 * w + 1]);
-            const uint32_t pk = pack2(p0, p1);
-            pf[v][w] = pk;
-            if (w & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l1, false);
-            else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l0, false);
+            for (int pp = ks * NPAIR / KS; pp < (ks + 1) * NPAIR / KS; ++pp) {
+              const int v = pp >> 2, w = pp & 3;
+              const float p0 = __builtin_amdgcn_exp2f(scur[8 * v + 2 * w]);
+              const float p1 = __builtin_amdgcn_exp2f(scur[8 * v + 2 * w + 1]);
+              const uint32_t pk = pack2(p0, p1);
+              pf[v][w] = pk;
+              if (w & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l1, false);
+              else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l0, false);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_barrier(0);
+          ls = l0 + l1;
         }
-        ls = l0 + l1;
-      }
-      check(scur, pf, ls);
-      __builtin_amdgcn_sched_barrier(0);
-      // region B (with the shift of tile j+1's scores)
-      pv(std::integral_constant<int, sl>{}, pf);
-      shift(snext);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);  // LDS read
+        check(scur, pf, ls);
+        __builtin_amdgcn_sched_barrier(0);
+        // region B (with the shift of tile j+1's scores)
+        pv(std::integral_constant<int, sl>{}, pf);
+        shift(snext);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);  // LDS read
 #pragma unroll
-      for (int i = 0; i < 2 * DB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 16 / (2 * DB), 1);  // VALU
-        if (i + 3 < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
+        for (int i = 0; i < 2 * DB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 16 / (2 * DB), 1);  // VALU
+          if (i + 3 < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mask(j + 1, snext);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      mask(j + 1, snext);
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(kIssuePerStep) : "memory");
       if (j == j_clip) {  // V(j+1) has landed: clear its keys past the end
         clip_tail((sl + 1) & 3);
@@ -553,6 +559,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     };
     // The last tile: weights, check and P V with the sequence-end clip; nothing to issue.
     auto last = [&](f32x16& scur) {
+      if (!wave_rows) return;
       weights(scur, pf, ls);
       check(scur, pf, ls);
       pv(std::integral_constant<int, 0>{}, pf);

@@ -25,6 +25,7 @@ constexpr int kCombineRows = 32;         // rows per combine task of split chunk
 constexpr int kXcds = 8;  // accelerator dies (own L2 each); a launch's workgroups are dealt to them round-robin
 constexpr int kSplitRows = 16;    // split path: rows of one 16-row MFMA block
 constexpr int kSplitMaxRows = 32; // split path: at most this many rows (two blocks per wave)
+constexpr int kFewRows = 2 * kRowsPerWave;  // chunk tiles of at most this many rows are cut into split-length key pieces
 
 // Per-request metadata copied to the workspace.
 struct SeqInfo {

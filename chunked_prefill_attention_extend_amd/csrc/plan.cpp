@@ -174,7 +174,7 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
     // of kWaves tiles, between kSplitKeysMin and kSplitKeysMax.
     int64_t split_keys = 0;
     for (int32_t r = 0; r < num_seqs; ++r)
-      if (int64_t(extend[r]) * group <= kSplitMaxRows) split_keys += (int64_t(prefix[r]) + extend[r]) * hkv;
+      if (int64_t(extend[r]) * group <= kFewRows) split_keys += (int64_t(prefix[r]) + extend[r]) * hkv;
     constexpr int64_t kGrain = int64_t(kSplitTile) * kWaves;
     int64_t piece = (split_keys + kSplitTargetItems - 1) / kSplitTargetItems;
     piece = (piece + kGrain - 1) / kGrain * kGrain;
@@ -223,7 +223,10 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
             const int64_t pos_max = (row0 + nrows - 1) / group;
             const int64_t key_end = int64_t(prefix[r]) + pos_max + 1;
             const int64_t ktiles = (key_end + kChunkKeys - 1) / kChunkKeys;
-            const int64_t pieces = std::max<int64_t>(1, std::min<int64_t>(chunk_pieces, key_end / kChunkMinPieceKeys));
+            int64_t pieces = std::max<int64_t>(1, std::min<int64_t>(chunk_pieces, key_end / kChunkMinPieceKeys));
+            // tiles of few rows (verify rows past the split path's reach, ragged last
+            // tiles) stream their keys like split items: pieces of the split length
+            if (nrows <= kFewRows) pieces = std::max<int64_t>(pieces, (key_end + piece - 1) / piece);
             if (pieces == 1) {
               add_chunk(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), 0, int32_t(key_end), -1, -1,
                                  {0, 0, 0}},

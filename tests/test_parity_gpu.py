@@ -110,7 +110,14 @@ def test_timed_variant_same_results_and_sane_stamps():
     extend = [e for _, e in launches]
     _, st, hz = ext.extend_attention(qd, cache.k, cache.v, cache.bt, prefix, extend, w.scale, o2, l2, timed=True)
     torch.cuda.synchronize()
-    assert torch.equal(out, o2) and torch.equal(lse, l2), "timed launch changed the results"
+    if not (torch.equal(out, o2) and torch.equal(lse, l2)):
+        d = (out.float() - o2.float()).abs()
+        rows = torch.nonzero(d.nan_to_num(1e9).amax(dim=(1, 2)) > 0).flatten().tolist()
+        dl = (lse - l2).abs().nan_to_num(1e9)
+        lrows = torch.nonzero(dl.amax(dim=1) > 0).flatten().tolist()
+        raise AssertionError(f"timed launch changed the results: out rows {rows[:16]} ({len(rows)}), max "
+                             f"{float(d.nan_to_num(1e9).max())}, NaN {int(torch.isnan(out.float()).sum())}/"
+                             f"{int(torch.isnan(o2.float()).sum())}; lse rows {lrows[:16]} ({len(lrows)})")
     st = st.cpu().numpy()
     assert hz > 0 and st.shape[1] == 4 and st.shape[0] > 0
     assert (st[:, 1] >= st[:, 0]).all() and (st[:, 0] > 0).all()
