@@ -50,9 +50,10 @@ constexpr int64_t kChunkLeadPct = 30;
 // accelerator dies (workgroup b to die b % kXcds, each die with its own L2) and
 // dispatched in order within a die, so the list is built as kXcds lanes, one per
 // die, read out round-robin:
-//  * each chunk group (tiles sharing one K/V range) goes whole to one lane, the
-//    longest groups first to the lane with the least chunk work, its tiles
-//    consecutive so that they run side by side and read the K/V into L2 once;
+//  * the chunk groups (tiles sharing one K/V range), longest first, are laid end
+//    to end and dealt to the lanes as contiguous runs of equal length, so that a
+//    group's tiles sit on one lane (or a few adjacent ones), consecutive, run side
+//    by side and read their K/V into that die's L2 once;
 //  * split items (decode / verify rows), longest first, fill the lanes to equal
 //    item counts, each to the lane with the most room and then the least work;
 //  * within a lane the chunk and split items are interleaved so that both kinds
@@ -80,16 +81,22 @@ static void order_items(std::vector<std::vector<WorkItem>>& groups, std::vector<
   std::vector<size_t> gorder(groups.size());
   for (size_t i = 0; i < gorder.size(); ++i) gorder[i] = i;
   std::stable_sort(gorder.begin(), gorder.end(), [&](size_t a, size_t b) { return gwork[a] > gwork[b]; });
-  size_t n_total = split_items.size();
-  for (size_t gi : gorder) {
-    size_t best = 0;
-    for (size_t l = 1; l < lanes.size(); ++l)
-      if (lanes[l].cwork < lanes[best].cwork ||
-          (lanes[l].cwork == lanes[best].cwork && lanes[l].chunk.size() < lanes[best].chunk.size()))
-        best = l;
-    lanes[best].chunk.insert(lanes[best].chunk.end(), groups[gi].begin(), groups[gi].end());
-    lanes[best].cwork += gwork[gi];
-    n_total += groups[gi].size();
+  // The groups, longest first, one after the other, dealt to the lanes as contiguous
+  // runs of equal length: a group lands on one lane or on a few adjacent ones, and
+  // every lane gets the same number of chunk items (the read-out below only maps
+  // list positions to dies while the lanes are equally long).
+  std::vector<WorkItem> all_chunk;
+  for (size_t gi : gorder) all_chunk.insert(all_chunk.end(), groups[gi].begin(), groups[gi].end());
+  size_t n_total = split_items.size() + all_chunk.size();
+  {
+    const size_t per = all_chunk.size() / lanes.size(), extra = all_chunk.size() % lanes.size();
+    size_t at = 0;
+    for (size_t l = 0; l < lanes.size(); ++l) {
+      const size_t cnt = per + (l < extra ? 1 : 0);
+      lanes[l].chunk.assign(all_chunk.begin() + at, all_chunk.begin() + at + cnt);
+      for (const WorkItem& x : lanes[l].chunk) lanes[l].cwork += chunk_work(x);
+      at += cnt;
+    }
   }
   std::stable_sort(split_items.begin(), split_items.end(),
                    [&](const WorkItem& x, const WorkItem& y) { return split_work(x) > split_work(y); });
