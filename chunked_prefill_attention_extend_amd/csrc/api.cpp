@@ -191,7 +191,8 @@ int extattn_workspace_bytes(int32_t num_seqs, const int32_t* prefix_lens, const 
   if (rc != EXTATTN_OK) return rc;
   Plan plan;  // sized with the fused append's items too, so one size serves both calls
   rc = build_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, plan, true);
-  if (rc != EXTATTN_OK) return fail(rc, "planning failed");
+  if (rc != EXTATTN_OK)
+    return fail(rc, rc == EXTATTN_ENOSPC ? "launch too large: partial results exceed 2^31 floats" : "planning failed");
   *bytes = plan.bytes;
   g_error.clear();
   return EXTATTN_OK;
@@ -272,7 +273,8 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
   if (fused && (!k_new || !v_new)) return fail(EXTATTN_EINVAL, "null k_new / v_new");
   Plan plan;
   rc = build_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, plan, fused);
-  if (rc != EXTATTN_OK) return fail(rc, "planning failed");
+  if (rc != EXTATTN_OK)
+    return fail(rc, rc == EXTATTN_ENOSPC ? "launch too large: partial results exceed 2^31 floats" : "planning failed");
   if (workspace_bytes < plan.bytes) return fail(EXTATTN_ENOSPC, "workspace too small");
   if (timed) {
     if (!n_items || !tick_hz) return fail(EXTATTN_EINVAL, "null n_items or tick_hz");

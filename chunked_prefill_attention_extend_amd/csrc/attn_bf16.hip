@@ -114,7 +114,7 @@ __device__ inline void softmax_step(f32x16 (&s)[NKB], f32x16 (&o)[DB], float& m,
 // slot (fp32 o normalised, natural-log lse) for the combine kernel.
 template <int D>
 __device__ inline void write_row(const AttnArgs& a, const f32x16 (&o)[D / 32], float m, float l, bool valid,
-                                 int hi, int64_t orow, int32_t slot, int rloc) {
+                                 int hi, int64_t orow, int32_t slot, int32_t slot_rows, int rloc) {
   constexpr int DB = D / 32;
   const float lt = l + __shfl_xor(l, 32);
   if (!valid) return;
@@ -132,7 +132,7 @@ __device__ inline void write_row(const AttnArgs& a, const f32x16 (&o)[D / 32], f
       }
     if (hi == 0 && a.lse) a.lse[orow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
   } else {
-    float* sl = a.slots + slot;  // rows [kRowsPerTile][D], then lse [kRowsPerTile]
+    float* sl = a.slots + slot;  // rows [slot_rows][D], then lse [slot_rows]
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -142,7 +142,7 @@ __device__ inline void write_row(const AttnArgs& a, const f32x16 (&o)[D / 32], f
         float4 v = {o[db][4 * u] * inv, o[db][4 * u + 1] * inv, o[db][4 * u + 2] * inv, o[db][4 * u + 3] * inv};
         *reinterpret_cast<float4*>(sl + rloc * D + d) = v;
       }
-    if (hi == 0) sl[kRowsPerTile * D + rloc] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    if (hi == 0) sl[slot_rows * D + rloc] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -577,7 +577,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     last(sa);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads issued past the end
   }
-  write_row<D>(a, o, m, l, valid, hi, orow, it.slot, rloc);
+  write_row<D>(a, o, m, l, valid, hi, orow, it.slot, it.slot_rows, rloc);
 }
 
 // ---------------------------------------------------------------------------

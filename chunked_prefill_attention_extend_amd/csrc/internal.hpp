@@ -57,7 +57,8 @@ struct WorkItem {
   int32_t key_end;
   int32_t slot;       // < 0: write out/lse directly; else float offset of this item's partial slot
   int32_t task;       // combine task that merges this item's slot, or -1 (direct write)
-  int32_t pad[3];
+  int32_t slot_rows;  // rows of the partial slot (a multiple of 16; 0 for direct writes)
+  int32_t pad[2];
 };
 
 // Merge of the partial results of rows [row0, row0 + nrows) of one (request, KV

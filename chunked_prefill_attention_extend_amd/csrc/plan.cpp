@@ -212,7 +212,8 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
             const int64_t kb = w * piece;
             const int64_t ke = std::min<int64_t>(kv_len, kb + piece);
             split_items.push_back(WorkItem{kItemSplit, r, g, 0, int32_t(rows), int32_t(kb), int32_t(ke),
-                                           int32_t(nwg > 1 ? slot0 + w * sf : -1), task, {0, 0, 0}});
+                                           int32_t(nwg > 1 ? slot0 + w * sf : -1), task, nwg > 1 ? srows : 0,
+                                           {0, 0}});
           }
           if (nwg > 1) {
             plan.tasks.push_back(CombineTask{r, g, 0, int32_t(rows), int32_t(slot0), int32_t(nwg), int32_t(sf),
@@ -222,7 +223,6 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
         }
       } else {
         const int64_t ntiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
-        const int64_t sf = int64_t(slot_floats(kRowsPerTile, head_dim));
         for (int32_t g = 0; g < hkv; ++g) {
           for (int64_t t = 0; t < ntiles; ++t) {
             const int64_t row0 = t * kRowsPerTile;
@@ -235,25 +235,29 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
             // tiles) stream their keys like split items: pieces of the split length
             if (nrows <= kFewRows) pieces = std::max<int64_t>(pieces, (key_end + piece - 1) / piece);
             if (pieces == 1) {
-              add_chunk(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), 0, int32_t(key_end), -1, -1,
-                                 {0, 0, 0}},
+              add_chunk(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), 0, int32_t(key_end), -1, -1, 0,
+                                 {0, 0}},
                         0);
               continue;
             }
-            // pieces of about equal tile counts; the last one holds the diagonal
+            // pieces of about equal tile counts; the last one holds the diagonal. A
+            // partial slot holds the tile's rows rounded up to 16 (not a whole tile:
+            // a few-row tile may have many pieces)
+            const int32_t srows = int32_t((nrows + 15) / 16 * 16);
+            const int64_t sf = int64_t(slot_floats(srows, head_dim));
             const int64_t slot0 = plan.n_slot_floats;
             const int32_t task0 = int32_t(plan.tasks.size());
             for (int64_t i = 0; i < pieces; ++i) {
               const int64_t kb = ktiles * i / pieces * kChunkKeys;
               const int64_t ke = i + 1 < pieces ? ktiles * (i + 1) / pieces * kChunkKeys : key_end;
               add_chunk(WorkItem{kItemChunk, r, g, int32_t(row0), int32_t(nrows), int32_t(kb), int32_t(ke),
-                                 int32_t(slot0 + i * sf), task0, {0, 0, 0}},
+                                 int32_t(slot0 + i * sf), task0, srows, {0, 0}},
                         i);
             }
             for (int64_t sr = 0; sr < nrows; sr += kCombineRows)
               plan.tasks.push_back(CombineTask{r, g, int32_t(row0 + sr),
                                                int32_t(std::min<int64_t>(kCombineRows, nrows - sr)), int32_t(slot0),
-                                               int32_t(pieces), int32_t(sf), kRowsPerTile, int32_t(sr), {0, 0, 0}});
+                                               int32_t(pieces), int32_t(sf), srows, int32_t(sr), {0, 0, 0}});
             plan.n_slot_floats += pieces * sf;
           }
         }
@@ -266,13 +270,15 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
       std::vector<WorkItem> app;
       for (int32_t r = 0; r < num_seqs; ++r)
         for (int32_t t = 0; t < extend[r]; t += kAppendTokens)
-          app.push_back(WorkItem{kItemAppend, r, 0, t, std::min(kAppendTokens, extend[r] - t), 0, 0, -1, -1,
-                                 {0, 0, 0}});
+          app.push_back(WorkItem{kItemAppend, r, 0, t, std::min(kAppendTokens, extend[r] - t), 0, 0, -1, -1, 0,
+                                 {0, 0}});
       plan.n_append = int32_t(app.size());
       plan.items.insert(plan.items.begin(), app.begin(), app.end());
     }
   }
 
+  // slot offsets travel as int32 floats
+  if (plan.n_slot_floats > INT32_MAX) return EXTATTN_ENOSPC;
   size_t off = kHeaderBytes;
   plan.off_zero = off;
   off += kZeroPageBytes;

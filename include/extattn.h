@@ -160,7 +160,8 @@ int extattn_chunk_plan(int64_t n_tokens, int64_t chunk_size, double hit_rate,
  * Workspace bytes that extattn_extend_attention needs for these requests
  * (host only). Arguments as for extattn_extend_attention. The result depends
  * only on the lengths, head counts, head_dim and dtype. Errors as for
- * extattn_extend_attention's argument checks.
+ * extattn_extend_attention's argument checks, and EXTATTN_ENOSPC when the
+ * launch's partial results would exceed 2^31 - 1 floats.
  */
 int extattn_workspace_bytes(int32_t num_seqs, const int32_t* prefix_lens, const int32_t* extend_lens,
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -225,7 +226,8 @@ int extattn_kv_append(const void* k_new, const void* v_new, void* k_cache, void*
  * extend < 1 or prefix < 0, Hq % Hkv != 0, a request needing more than
  * max_blocks blocks, a non-finite or non-positive scale, sum(E) above 2^31-1;
  * EXTATTN_EUNSUPPORTED for head_dim, block_size or dtype; EXTATTN_ENOSPC for a
- * small workspace; EXTATTN_EHIP on a HIP failure.
+ * small workspace or a launch whose partial results exceed 2^31 - 1 floats;
+ * EXTATTN_EHIP on a HIP failure.
  */
 int extattn_extend_attention(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_table, int32_t max_blocks, int64_t num_blocks,

@@ -86,7 +86,9 @@ static bool check_launch(const std::vector<int32_t>& P, const std::vector<int32_
     }
     if (x.slot >= 0) {
       CHECK(x.task >= 0 && size_t(x.task) < plan.tasks.size(), "seed %u: item %zu task", seed, i);
-      const int srows = x.kind == kItemChunk ? kRowsPerTile : (rows <= kSplitRows ? kSplitRows : kSplitMaxRows);
+      const int srows = x.kind == kItemChunk ? (x.nrows + 15) / 16 * 16 : (rows <= kSplitRows ? kSplitRows : kSplitMaxRows);
+      CHECK(x.slot_rows == srows, "seed %u: item %zu slot of %d rows, expected %d", seed, i, x.slot_rows, srows);
+      CHECK(x.slot % 4 == 0, "seed %u: item %zu slot not 16-byte aligned", seed, i);
       slots.push_back({x.slot, x.slot + int64_t(slot_floats(srows, d))});
     } else {
       CHECK(x.task < 0, "seed %u: direct item %zu has a task", seed, i);
@@ -126,6 +128,7 @@ static bool check_launch(const std::vector<int32_t>& P, const std::vector<int32_
     for (int i = 0; i < t.nslots; ++i)
       CHECK(slot_starts.count(int64_t(t.slot0) + int64_t(i) * t.stride), "seed %u: task reads an unwritten slot", seed);
     CHECK(t.srow0 + t.nrows <= t.slot_rows, "seed %u: task rows past the slot", seed);
+    CHECK(int64_t(t.stride) == int64_t(slot_floats(t.slot_rows, d)), "seed %u: task stride %d", seed, t.stride);
     for (int rr = t.row0; rr < t.row0 + t.nrows; ++rr) ++merged[{t.seq, t.kv_head, rr}];
   }
   for (auto& kv : ranges) {
