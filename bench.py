@@ -284,6 +284,35 @@ def verify_rows_sweep(torch, ext, synth, reps: int = 10):
             "rows": rows}
 
 
+def host_planning(ext, synth, n: int = 200):
+    """Host time of planning a launch (workspace_bytes), planned afresh with the plan
+    table off against a table hit, for the mixed step and the sweep's last chunk."""
+    w = synth.make_workload("mixed_budget2048")
+    shapes = {"mixed_budget2048": ([r.launch[0] for r in w.requests], [r.launch[1] for r in w.requests], 32, 8),
+              "sweep128k_t127": ([130048], [1024], 64, 8)}
+    import ctypes
+    lib = ext.load_library()
+    res = {}
+    for name, (p, e, hq, hkv) in shapes.items():
+        pa, ea = np.asarray(p, dtype=np.int32), np.asarray(e, dtype=np.int32)
+        pp, ep = pa.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ea.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        out = ctypes.c_size_t()
+        row = {}
+        for mode, entries in (("planned_us", 0), ("table_hit_us", 256)):
+            ext.plan_cache_configure(entries)
+            lib.extattn_workspace_bytes(len(pa), pp, ep, hq, hkv, 128, ext.EXTATTN_BF16, ctypes.byref(out))
+            t0 = time.perf_counter()
+            for _ in range(n):
+                lib.extattn_workspace_bytes(len(pa), pp, ep, hq, hkv, 128, ext.EXTATTN_BF16, ctypes.byref(out))
+            row[mode] = (time.perf_counter() - t0) / n * 1e6
+        res[name] = row
+    ext.plan_cache_configure(256)
+    ext.plan_cache_clear()
+    res["note"] = ("one C-ABI call (ctypes) per launch shape; the attention call after sizing reuses the "
+                   "record, so with the table a sized launch plans once")
+    return res
+
+
 def calibration(torch):
     """Reference rates on this GPU, for reading the rooflines: a vendor bf16 GEMM on
     random data (the practical matrix-core rate, which sits below the published dense
@@ -605,6 +634,7 @@ def main() -> int:
         verify = verify_rows_sweep(torch, ext, synth)
     log("calibration")
     calib = calibration(torch)
+    planning = host_planning(ext, synth)
     base = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
@@ -633,6 +663,7 @@ def main() -> int:
         "sweep_attention": {"aggregate_tflops": aggregate, "per_chunk_tflops": per_chunk,
                             "note": "attention launches only (kv_append excluded); sum(F) / sum(per-chunk median)"},
         "calibration": calib,
+        "host_planning": planning,
         "fused_append_step": fused,
         "mixed_step": mixed,
         "verify_rows": verify,

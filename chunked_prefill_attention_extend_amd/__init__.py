@@ -16,6 +16,9 @@ from .binding import (  # noqa: F401
     kv_append,
     load_library,
     mixed_chunk_step,
+    plan_cache_clear,
+    plan_cache_configure,
+    plan_cache_stats,
     token_budget_step,
     workspace_bytes,
 )

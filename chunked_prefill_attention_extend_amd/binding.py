@@ -76,6 +76,12 @@ def load_library() -> ctypes.CDLL:
     lib.extattn_extend_attention_timed.restype = ctypes.c_int
     lib.extattn_extend_attention_timed.argtypes = [*lib.extattn_extend_attention.argtypes, ctypes.c_void_p,
                                                    ctypes.c_int32, _c_i32p, ctypes.POINTER(ctypes.c_double)]
+    lib.extattn_plan_cache_configure.restype = ctypes.c_int
+    lib.extattn_plan_cache_configure.argtypes = [ctypes.c_int32, ctypes.c_int64]
+    lib.extattn_plan_cache_stats.restype = ctypes.c_int
+    lib.extattn_plan_cache_stats.argtypes = [_c_i64p, _c_i64p, _c_i32p, _c_i64p]
+    lib.extattn_plan_cache_clear.restype = ctypes.c_int
+    lib.extattn_plan_cache_clear.argtypes = []
     _lib = lib
     return lib
 
@@ -223,6 +229,25 @@ def workspace_bytes(prefix_lens, extend_lens, num_q_heads: int, num_kv_heads: in
     _check(lib.extattn_workspace_bytes(len(p), _ptr(p), _ptr(e), num_q_heads, num_kv_heads, head_dim,
                                        dtype_code, ctypes.byref(out)))
     return out.value
+
+
+def plan_cache_configure(max_entries: int, max_bytes: int = 64 << 20) -> None:
+    """Bound the library's launch-plan table (0 entries turns it off)."""
+    _check(load_library().extattn_plan_cache_configure(int(max_entries), int(max_bytes)))
+
+
+def plan_cache_stats() -> dict:
+    """Hits and misses since the last clear, records held and their host bytes."""
+    h, m, b = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    n = ctypes.c_int32()
+    _check(load_library().extattn_plan_cache_stats(ctypes.byref(h), ctypes.byref(m), ctypes.byref(n),
+                                                   ctypes.byref(b)))
+    return {"hits": h.value, "misses": m.value, "entries": n.value, "bytes": b.value}
+
+
+def plan_cache_clear() -> None:
+    """Drop every launch-plan record and zero the counters."""
+    _check(load_library().extattn_plan_cache_clear())
 
 
 def _stream_handle(stream) -> int:

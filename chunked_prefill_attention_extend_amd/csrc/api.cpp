@@ -189,11 +189,33 @@ int extattn_workspace_bytes(int32_t num_seqs, const int32_t* prefix_lens, const 
   if (!bytes) return fail(EXTATTN_EINVAL, "bytes must not be null");
   int rc = check_common(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, true);
   if (rc != EXTATTN_OK) return rc;
-  Plan plan;  // sized with the fused append's items too, so one size serves both calls
-  rc = build_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, plan, true);
+  // the launch plan holds the fused append's items too, so one size serves both calls;
+  // it is kept in the plan cache for the attention call that follows
+  std::shared_ptr<const LaunchPlan> lp;
+  rc = get_launch_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, lp);
   if (rc != EXTATTN_OK)
     return fail(rc, rc == EXTATTN_ENOSPC ? "launch too large: partial results exceed 2^31 floats" : "planning failed");
-  *bytes = plan.bytes;
+  *bytes = lp->plan.bytes;
+  g_error.clear();
+  return EXTATTN_OK;
+}
+
+int extattn_plan_cache_configure(int32_t max_entries, int64_t max_bytes) {
+  if (max_entries < 0 || max_bytes < 0) return fail(EXTATTN_EINVAL, "plan cache bounds must be >= 0");
+  plan_cache_configure(max_entries, max_bytes);
+  g_error.clear();
+  return EXTATTN_OK;
+}
+
+int extattn_plan_cache_stats(int64_t* hits, int64_t* misses, int32_t* entries, int64_t* bytes) {
+  if (!hits || !misses || !entries || !bytes) return fail(EXTATTN_EINVAL, "null output pointer");
+  plan_cache_stats(hits, misses, entries, bytes);
+  g_error.clear();
+  return EXTATTN_OK;
+}
+
+int extattn_plan_cache_clear(void) {
+  plan_cache_clear();
   g_error.clear();
   return EXTATTN_OK;
 }
@@ -271,15 +293,19 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
   if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(EXTATTN_EINVAL, "scale must be finite and > 0");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(EXTATTN_EINVAL, "workspace must be 256-byte aligned");
   if (fused && (!k_new || !v_new)) return fail(EXTATTN_EINVAL, "null k_new / v_new");
-  Plan plan;
-  rc = build_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, plan, fused);
+  std::shared_ptr<const LaunchPlan> lp;
+  rc = get_launch_plan(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, lp);
   if (rc != EXTATTN_OK)
     return fail(rc, rc == EXTATTN_ENOSPC ? "launch too large: partial results exceed 2^31 floats" : "planning failed");
+  const Plan& plan = lp->plan;
   if (workspace_bytes < plan.bytes) return fail(EXTATTN_ENOSPC, "workspace too small");
+  // the plan lists the fused append's items first; a plain launch starts after them
+  const int32_t first = fused ? 0 : plan.n_append;
+  const int32_t n_launch = int32_t(plan.items.size()) - first;
   if (timed) {
     if (!n_items || !tick_hz) return fail(EXTATTN_EINVAL, "null n_items or tick_hz");
     if (dtype != EXTATTN_BF16) return fail(EXTATTN_EUNSUPPORTED, "timed launches exist for bf16 only");
-    *n_items = int32_t(plan.items.size());
+    *n_items = n_launch;
     int dev = 0, khz = 0;
     hipError_t he = hipGetDevice(&dev);
     if (he == hipSuccess) he = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
@@ -289,14 +315,8 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
     if (!stamps) return fail(EXTATTN_EINVAL, "null stamps");
   }
 
-  std::vector<unsigned char> blob(plan.upload_bytes, 0);
-  std::memcpy(blob.data() + plan.off_seqs, plan.seqs.data(), sizeof(SeqInfo) * plan.seqs.size());
-  if (!plan.items.empty())
-    std::memcpy(blob.data() + plan.off_items, plan.items.data(), sizeof(WorkItem) * plan.items.size());
-  if (!plan.tasks.empty())
-    std::memcpy(blob.data() + plan.off_tasks, plan.tasks.data(), sizeof(CombineTask) * plan.tasks.size());
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  rc = upload(blob.data(), blob.size(), workspace, st);
+  rc = upload(lp->blob.data(), lp->blob.size(), workspace, st);
   if (rc != EXTATTN_OK) return rc;
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -308,7 +328,7 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
   a.out = out;
   a.lse = lse;
   a.seqs = reinterpret_cast<const SeqInfo*>(ws + plan.off_seqs);
-  a.items = reinterpret_cast<const WorkItem*>(ws + plan.off_items);
+  a.items = reinterpret_cast<const WorkItem*>(ws + plan.off_items) + first;
   a.tasks = reinterpret_cast<const CombineTask*>(ws + plan.off_tasks);
   a.slots = reinterpret_cast<float*>(ws + plan.off_slots);
   a.err = reinterpret_cast<int32_t*>(ws);
@@ -323,7 +343,7 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.total_rows = int32_t(plan.total_rows);
-  a.n_items = int32_t(plan.items.size());
+  a.n_items = n_launch;
   a.n_tasks = int32_t(plan.tasks.size());
   a.stamps = timed ? stamps : nullptr;
   if (fused) {

@@ -5,6 +5,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <memory>
 #include <vector>
 
 namespace extattn {
@@ -152,6 +153,23 @@ constexpr size_t kZeroPageBytes = size_t(kBlockSize) * 128 * 4;  // one (block, 
 // plan.cpp
 int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
                int32_t head_dim, int32_t dtype, Plan& plan, bool with_append = false);
+
+// plan_cache.cpp. A launch's plan (built with the fused append's items first, so
+// one record serves the plain and the fused launch: the plain one starts at item
+// n_append) and the workspace image up to plan.upload_bytes.
+struct LaunchPlan {
+  Plan plan;
+  std::vector<unsigned char> blob;
+};
+constexpr int32_t kPlanCacheEntries = 256;       // default table bounds
+constexpr int64_t kPlanCacheBytes = 64ll << 20;
+int make_launch_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
+                     int32_t head_dim, int32_t dtype, LaunchPlan& lp);
+int get_launch_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
+                    int32_t head_dim, int32_t dtype, std::shared_ptr<const LaunchPlan>& out);
+void plan_cache_configure(int32_t max_entries, int64_t max_bytes);
+void plan_cache_stats(int64_t* hits, int64_t* misses, int32_t* entries, int64_t* bytes);
+void plan_cache_clear();
 
 // budget.cpp
 int token_budget_step_impl(int32_t n_running, const int64_t* running_total, const int64_t* running_computed,

@@ -65,18 +65,34 @@ constexpr int64_t kChunkLeadPct = 30;
 // Work is estimated as rows x keys for a chunk item and keys for a split item.
 static void order_items(std::vector<std::vector<WorkItem>>& groups, std::vector<WorkItem>& split_items,
                         std::vector<WorkItem>& out) {
-  auto chunk_work = [](const WorkItem& x) { return int64_t(x.key_end - x.key_begin) * x.nrows; };
-  auto split_work = [](const WorkItem& x) { return int64_t(x.key_end - x.key_begin); };
-  struct Lane {
-    std::vector<WorkItem> chunk, split;
-    int64_t cwork = 0, swork = 0;
-  };
-  std::vector<Lane> lanes(kXcds);
+  // Items are moved by index (into `pool`: the chunk groups' items, then the split
+  // items) and gathered once at the end.
+  std::vector<WorkItem> pool;
+  std::vector<int64_t> work;
+  std::vector<std::pair<uint32_t, uint32_t>> granges;  // [begin, end) in pool
+  size_t n_chunk = 0;
+  for (const auto& g : groups) n_chunk += g.size();
+  const size_t n_total = n_chunk + split_items.size();
+  pool.reserve(n_total);
+  work.reserve(n_total);
+  for (const auto& g : groups) {
+    granges.push_back({uint32_t(pool.size()), uint32_t(pool.size() + g.size())});
+    for (const WorkItem& x : g) {
+      pool.push_back(x);
+      work.push_back(int64_t(x.key_end - x.key_begin) * x.nrows);
+    }
+  }
+  for (const WorkItem& x : split_items) {
+    pool.push_back(x);
+    work.push_back(int64_t(x.key_end - x.key_begin));
+  }
+  std::vector<uint32_t> idx(n_total);
+  for (size_t i = 0; i < n_total; ++i) idx[i] = uint32_t(i);
+  auto by_work = [&](uint32_t a, uint32_t b) { return work[a] > work[b]; };
   std::vector<int64_t> gwork(groups.size(), 0);
   for (size_t i = 0; i < groups.size(); ++i) {
-    std::stable_sort(groups[i].begin(), groups[i].end(),
-                     [&](const WorkItem& x, const WorkItem& y) { return chunk_work(x) > chunk_work(y); });
-    for (const WorkItem& x : groups[i]) gwork[i] += chunk_work(x);
+    std::stable_sort(idx.begin() + granges[i].first, idx.begin() + granges[i].second, by_work);
+    for (uint32_t k = granges[i].first; k < granges[i].second; ++k) gwork[i] += work[k];
   }
   std::vector<size_t> gorder(groups.size());
   for (size_t i = 0; i < gorder.size(); ++i) gorder[i] = i;
@@ -85,47 +101,61 @@ static void order_items(std::vector<std::vector<WorkItem>>& groups, std::vector<
   // runs of equal length: a group lands on one lane or on a few adjacent ones, and
   // every lane gets the same number of chunk items (the read-out below only maps
   // list positions to dies while the lanes are equally long).
-  std::vector<WorkItem> all_chunk;
-  for (size_t gi : gorder) all_chunk.insert(all_chunk.end(), groups[gi].begin(), groups[gi].end());
-  size_t n_total = split_items.size() + all_chunk.size();
+  std::vector<uint32_t> all_chunk;
+  all_chunk.reserve(n_chunk);
+  for (size_t gi : gorder)
+    all_chunk.insert(all_chunk.end(), idx.begin() + granges[gi].first, idx.begin() + granges[gi].second);
+  struct Lane {
+    size_t c0 = 0, c1 = 0;  // chunk items all_chunk[c0, c1)
+    std::vector<uint32_t> split;
+    int64_t cwork = 0, swork = 0;
+  };
+  std::vector<Lane> lanes(kXcds);
   {
-    const size_t per = all_chunk.size() / lanes.size(), extra = all_chunk.size() % lanes.size();
+    const size_t per = n_chunk / lanes.size(), extra = n_chunk % lanes.size();
     size_t at = 0;
     for (size_t l = 0; l < lanes.size(); ++l) {
-      const size_t cnt = per + (l < extra ? 1 : 0);
-      lanes[l].chunk.assign(all_chunk.begin() + at, all_chunk.begin() + at + cnt);
-      for (const WorkItem& x : lanes[l].chunk) lanes[l].cwork += chunk_work(x);
-      at += cnt;
+      lanes[l].c0 = at;
+      lanes[l].c1 = at + per + (l < extra ? 1 : 0);
+      for (size_t k = lanes[l].c0; k < lanes[l].c1; ++k) lanes[l].cwork += work[all_chunk[k]];
+      at = lanes[l].c1;
     }
   }
-  std::stable_sort(split_items.begin(), split_items.end(),
-                   [&](const WorkItem& x, const WorkItem& y) { return split_work(x) > split_work(y); });
+  std::stable_sort(idx.begin() + n_chunk, idx.end(), by_work);
   const int64_t target = int64_t((n_total + lanes.size() - 1) / lanes.size());
-  for (const WorkItem& x : split_items) {
-    size_t best = 0;
-    auto room = [&](size_t l) { return target - int64_t(lanes[l].chunk.size() + lanes[l].split.size()); };
-    for (size_t l = 1; l < lanes.size(); ++l)
-      if (room(l) > room(best) || (room(l) == room(best) && lanes[l].swork < lanes[best].swork)) best = l;
-    lanes[best].split.push_back(x);
-    lanes[best].swork += split_work(x);
+  int64_t room[kXcds], swork[kXcds];
+  for (int l = 0; l < kXcds; ++l) {
+    room[l] = target - int64_t(lanes[l].c1 - lanes[l].c0);
+    swork[l] = 0;
+    lanes[l].split.reserve(size_t(std::max<int64_t>(room[l], 0)));
   }
+  for (size_t k = n_chunk; k < n_total; ++k) {
+    const uint32_t x = idx[k];
+    int best = 0;
+    for (int l = 1; l < kXcds; ++l)
+      if (room[l] > room[best] || (room[l] == room[best] && swork[l] < swork[best])) best = l;
+    lanes[best].split.push_back(x);
+    --room[best];
+    swork[best] += work[x];
+  }
+  for (int l = 0; l < kXcds; ++l) lanes[l].swork = swork[l];
   // interleave within each lane
-  std::vector<std::vector<WorkItem>> seq(lanes.size());
+  std::vector<std::vector<uint32_t>> seq(lanes.size());
   for (size_t l = 0; l < lanes.size(); ++l) {
     const Lane& ln = lanes[l];
-    size_t ci = 0, si = 0;
+    seq[l].reserve(ln.c1 - ln.c0 + ln.split.size());
+    size_t ci = ln.c0, si = 0;
     int64_t cdone = 0, sdone = 0;
-    while (ci < ln.chunk.size() || si < ln.split.size()) {
+    while (ci < ln.c1 || si < ln.split.size()) {
       // next item from the list whose dispatched fraction (with the chunk lead) is smaller
       const bool take_chunk =
           si == ln.split.size() ||
-          (ci < ln.chunk.size() &&
-           __int128(cdone) * ln.swork * (100 - kChunkLeadPct) <= __int128(sdone) * ln.cwork * 100);
+          (ci < ln.c1 && __int128(cdone) * ln.swork * (100 - kChunkLeadPct) <= __int128(sdone) * ln.cwork * 100);
       if (take_chunk) {
-        cdone += chunk_work(ln.chunk[ci]);
-        seq[l].push_back(ln.chunk[ci++]);
+        cdone += work[all_chunk[ci]];
+        seq[l].push_back(all_chunk[ci++]);
       } else {
-        sdone += split_work(ln.split[si]);
+        sdone += work[ln.split[si]];
         seq[l].push_back(ln.split[si++]);
       }
     }
@@ -135,7 +165,7 @@ static void order_items(std::vector<std::vector<WorkItem>>& groups, std::vector<
   out.reserve(n_total);
   for (size_t k = 0; out.size() < n_total; ++k)
     for (size_t l = 0; l < seq.size(); ++l)
-      if (k < seq[l].size()) out.push_back(seq[l][k]);
+      if (k < seq[l].size()) out.push_back(pool[seq[l][k]]);
 }
 
 // Work list of one launch. Requests whose E * group rows fit two 16-row MFMA

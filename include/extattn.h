@@ -25,7 +25,9 @@
  *    NULL means the default stream) and the call returns without waiting;
  *    outputs are valid once the stream has reached that point. The library
  *    keeps pinned host staging buffers of its own for the small metadata it
- *    copies to the workspace (allocated on first use, reused afterwards).
+ *    copies to the workspace (allocated on first use, reused afterwards), and
+ *    a bounded host table of launch plans keyed by the launch's shape (see
+ *    extattn_plan_cache_configure).
  *  - Element types: EXTATTN_BF16 (bfloat16) or EXTATTN_F32 (float). q, the
  *    caches and out share one element type; lse is always float.
  *  - Heads: num_q_heads must be a multiple of num_kv_heads; query head h reads
@@ -166,6 +168,35 @@ int extattn_chunk_plan(int64_t n_tokens, int64_t chunk_size, double hit_rate,
 int extattn_workspace_bytes(int32_t num_seqs, const int32_t* prefix_lens, const int32_t* extend_lens,
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t dtype, size_t* bytes);
+
+/*
+ * Launch-plan cache (host only, thread-safe).
+ *
+ * The latency-table RFC (sections 3.1.3 and 3.1.4) keys the cost of one
+ * forward by its dynamic shape and fills a table once per distinct shape. The
+ * same idea here keys a launch's configuration: the work list, the combine
+ * tasks, the workspace layout and the metadata image uploaded to the workspace
+ * depend only on (dtype, num_q_heads, num_kv_heads, head_dim, and each
+ * request's (prefix_len, extend_len) in order). extattn_workspace_bytes,
+ * extattn_extend_attention, extattn_extend_attention_append and
+ * extattn_extend_attention_timed look the shape up and build the plan only on
+ * a miss; one record serves the plain and the fused-append call of a shape, so
+ * sizing the workspace and then launching plans once. Results never depend on
+ * whether a plan came from the table.
+ *
+ * extattn_plan_cache_configure: keep at most max_entries records using at most
+ *   max_bytes of host memory, least recently used first out (defaults 256
+ *   records, 64 MiB); max_entries = 0 turns the table off (every call plans).
+ *   Shrinking evicts at once. Errors: EXTATTN_EINVAL for negative bounds.
+ * extattn_plan_cache_stats: lookups that hit / missed since the last clear,
+ *   records held and their host bytes. Errors: EXTATTN_EINVAL for a null
+ *   output pointer.
+ * extattn_plan_cache_clear: drop every record and zero the counters (the
+ *   bounds stay). Records in use by a concurrent call stay valid for it.
+ */
+int extattn_plan_cache_configure(int32_t max_entries, int64_t max_bytes);
+int extattn_plan_cache_stats(int64_t* hits, int64_t* misses, int32_t* entries, int64_t* bytes);
+int extattn_plan_cache_clear(void);
 
 /* Workspace bytes that extattn_kv_append needs for num_seqs requests (host only). */
 size_t extattn_kv_append_workspace_bytes(int32_t num_seqs);

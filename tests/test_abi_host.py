@@ -133,3 +133,69 @@ def test_binding_rejects_device_lengths_and_bad_shapes():
     with pytest.raises(ValueError):
         ext.workspace_bytes([1, 2], [1], 8, 8, 128, 0)
     assert B._host_i32(torch.tensor([1, 2, 3])).tolist() == [1, 2, 3]
+
+
+@pytest.fixture
+def fresh_plan_cache():
+    ext.plan_cache_clear()
+    ext.plan_cache_configure(256, 64 << 20)
+    yield
+    ext.plan_cache_configure(256, 64 << 20)
+    ext.plan_cache_clear()
+
+
+def test_plan_cache_through_the_abi(fresh_plan_cache):
+    """Sizing a workspace plans once per shape; the table's bounds and counters."""
+    mixed = ([100, 2000, 5], [1, 300, 1])
+    size = ext.workspace_bytes(*mixed, 32, 8, 128, ext.EXTATTN_BF16)
+    assert ext.plan_cache_stats()["misses"] == 1 and ext.plan_cache_stats()["entries"] == 1
+    assert ext.workspace_bytes(*mixed, 32, 8, 128, ext.EXTATTN_BF16) == size
+    st = ext.plan_cache_stats()
+    assert st["hits"] == 1 and st["misses"] == 1 and st["bytes"] > 0
+    ext.workspace_bytes([100, 2000, 5], [1, 301, 1], 32, 8, 128, ext.EXTATTN_BF16)
+    ext.workspace_bytes(*mixed, 64, 8, 128, ext.EXTATTN_BF16)
+    assert ext.plan_cache_stats()["misses"] == 3
+    # off: same sizes, nothing kept
+    ext.plan_cache_configure(0)
+    assert ext.plan_cache_stats()["entries"] == 0
+    assert ext.workspace_bytes(*mixed, 32, 8, 128, ext.EXTATTN_BF16) == size
+    assert ext.plan_cache_stats()["entries"] == 0
+    with pytest.raises(ValueError):
+        ext.plan_cache_configure(-1)
+    lib = ext.load_library()
+    assert lib.extattn_plan_cache_stats(None, None, None, None) == B.EXTATTN_EINVAL
+    ext.plan_cache_clear()
+    assert ext.plan_cache_stats() == {"hits": 0, "misses": 0, "entries": 0, "bytes": 0}
+
+
+def test_plan_cache_many_threads_same_sizes(fresh_plan_cache):
+    """Concurrent sizing calls (ctypes drops the GIL) through a table smaller than the
+    set of shapes return what a cold, single-threaded call returns."""
+    import threading
+    rng = random.Random(11)
+    shapes = []
+    for i in range(20):
+        n = rng.randint(1, 8)
+        shapes.append(([rng.randint(0, 9000) + (i if j == 0 else 0) for j in range(n)],
+                       [rng.choice([1, 1, 3, 700]) for _ in range(n)]))
+    ext.plan_cache_configure(0)
+    want = [ext.workspace_bytes(p, e, 32, 8, 128, ext.EXTATTN_BF16) for p, e in shapes]
+    ext.plan_cache_configure(6)
+    ext.plan_cache_clear()
+    bad = []
+
+    def worker(seed):
+        r = random.Random(seed)
+        for _ in range(200):
+            i = r.randrange(len(shapes))
+            if ext.workspace_bytes(*shapes[i], 32, 8, 128, ext.EXTATTN_BF16) != want[i]:
+                bad.append(i)
+
+    th = [threading.Thread(target=worker, args=(s,)) for s in range(6)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not bad
+    st = ext.plan_cache_stats()
+    assert st["hits"] + st["misses"] == 1200 and st["entries"] <= 6
