@@ -75,7 +75,7 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate (staging)");
   }
   if (s.cap < bytes) {
-    if (s.host) hipHostFree(s.host);
+    if (s.host) (void)hipHostFree(s.host);
     s.host = nullptr;
     s.cap = 0;
     size_t cap = 1 << 16;

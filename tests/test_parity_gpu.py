@@ -92,6 +92,34 @@ def test_verify_rows_long_contexts():
     check_launch(sub, out, lse, q_off, q, what="verify rows, long contexts")
 
 
+def test_long_chunk_from_empty_prefix():
+    """The largest chunk of the pages' workloads and then some: one 32768-token prompt
+    from an empty cache (32 / 8 heads: 512 tiles per KV head, keys up to 32768),
+    compared on sampled rows spread over the whole chunk."""
+    w = custom_workload(4242, [(0, 32768)], 32, 8, 128)
+    log("long chunk: P=0, E=32768, 32/8 heads, D=128, sampled rows")
+    out, lse, q_off, q = run_launch(w)
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 16383, 32766, 32767], rng.choice(32768, 25, replace=False)]))
+    check_launch(w, out, lse, q_off, q, row_sample={0: rows}, what="long chunk")
+
+
+def test_many_decode_rows():
+    """300 decode rows in one launch (contexts 1..3000 tokens: 2400 split items, one
+    per request and KV head, many of them a single tile), 30 requests compared."""
+    rng = np.random.default_rng(77)
+    ctx = rng.integers(1, 3000, size=300, endpoint=True)
+    ctx[:3] = [1, 2, 3000]
+    launches = [(int(c - 1), 1) for c in ctx]
+    w = custom_workload(77, launches, 32, 8, 128)
+    log("many decode rows: 300 requests, context 1..3000, 32/8 heads, D=128")
+    out, lse, q_off, q = run_launch(w)
+    keep = set(range(3)) | set(rng.choice(np.arange(3, 300), 27, replace=False).tolist())
+    sub = custom_workload(77, launches, 32, 8, 128)
+    sub.requests = [r for r in sub.requests if r.index in keep]
+    check_launch(sub, out, lse, q_off, q, what="many decode rows")
+
+
 def test_timed_variant_same_results_and_sane_stamps():
     """The measurement variant gives bit-identical results and one
     {start, end, kind, request} record per work item."""
