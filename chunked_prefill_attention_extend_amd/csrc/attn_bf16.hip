@@ -244,6 +244,16 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + orow * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = valid ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : zero4();
+    // The softmax scale in log2 units goes into Q once (rounded to bf16, nearest even),
+    // so scores leave the product scaled. The rounding moves a score by about 2^-9 of
+    // its terms' spread, well below the effect of the weights' own bf16 rounding.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = qf[ks][e];
+        qf[ks][e] = pack2(__uint_as_float(u << 16) * c2, __uint_as_float(u & 0xffff0000u) * c2);
+      }
   }
 
   const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
@@ -336,6 +346,9 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   // sum l. m is the exact row max of the first tile; afterwards it is raised only
   // when a tile's weights grow past kSumBound (rare), so no tile needs a row max.
   float m = 0.f, l = 0.f;
+  // -m in every accumulator element: the QK product of a tile starts from it, so
+  // its scores come out shifted
+  f32x16 negm = f32x16{};
 
   // S^T of one tile from K ring slot `slot` (compile-time). Invalid blocks were
   // loaded from the zero page; keys past the sequence end are masked later.
@@ -368,11 +381,11 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
         if (key_of_elem(i, 0) > t) s[i] = -INFINITY;
     }
   };
-  // Scores are kept shifted, s c - m (log2 units), from the region after their QK
-  // product on. Weights p = 2^s as packed bf16 for the P.V product, and this lane's sum
-  // of them over the tile. The sum adds the same bf16 values (a dot product with
-  // ones), so the normalisation matches the numerator of P.V exactly.
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // Scores leave their QK product shifted, s c - m (log2 units): Q carries the scale
+  // and the product starts from -m. Weights p = 2^s as packed bf16 for the P.V
+  // product, and this lane's fp32 sum of them over the tile, taken before the
+  // rounding (lse stays exact up to fp32 arithmetic; the normaliser is within 2^-9
+  // relative of the rounded weights' sum).
   auto weights = [&](const f32x16& s, u32x4 (&pf)[2], float& ls) {
     float l0 = 0.f, l1 = 0.f;
 #pragma unroll
@@ -381,20 +394,17 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       for (int w = 0; w < 4; ++w) {
         const float p0 = __builtin_amdgcn_exp2f(s[8 * v + 2 * w]);
         const float p1 = __builtin_amdgcn_exp2f(s[8 * v + 2 * w + 1]);
-        // (the packed value goes through a local: a bit cast of a vector element
-        // lvalue such as pf[v][w] has been seen to read element 0)
-        const uint32_t pk = pack2(p0, p1);
-        pf[v][w] = pk;
-        if (w & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l1, false);
-        else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l0, false);
+        pf[v][w] = pack2(p0, p1);
+        l0 += p0;
+        l1 += p1;
       }
     ls = l0 + l1;
   };
   // Check of a tile's weights before they enter P.V: when some lane's sum passed
   // kSumBound (or overflowed), raise m by the rows' exact max over the (shifted)
-  // tile, rescale O and l, shift the tile again and redo its weights. The next
-  // tile's scores are shifted afterwards, with the new m. Then add the sum to l.
-  auto check = [&](f32x16& s, u32x4 (&pf)[2], float& ls) {
+  // tile, rescale O and l, shift the tile and the next one (already computed from
+  // the old m) again and redo the tile's weights. Then add the sum to l.
+  auto check = [&](f32x16& s, u32x4 (&pf)[2], float& ls, f32x16* snext) {
     if (__builtin_amdgcn_ballot_w64(ls > kSumBound) != 0) {
       float mx = row_max(s);
       mx = fmaxf(mx, partner(mx, hi));
@@ -406,13 +416,15 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       m += d;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] -= d;
+      if (snext) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) (*snext)[i] -= d;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negm[i] = -m;
       weights(s, pf, ls);
     }
     l += ls;
-  };
-  auto shift = [&](f32x16& s) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = fmaf(s[i], c2, -m);
   };
   // O^T += V^T P^T for one tile from V ring slot `slot` (compile-time).
   auto pv = [&](auto slot_tag, const u32x4 (&pf)[2]) {
@@ -476,17 +488,21 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     if (wave_rows) {
       qk(std::integral_constant<int, 0>{}, sa);
       mask(t0, sa);
-      float mx = row_max(sa) * c2;
+      float mx = row_max(sa);
       mx = fmaxf(mx, partner(mx, hi));
       m = (mx == -INFINITY) ? 0.f : mx;
-      shift(sa);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sa[i] -= m;
+        negm[i] = -m;
+      }
     }
     // Steady step u (tile j = t0 + u, not the last): S(j) is in scur (masked), K(j+1)
     // in K slot (u+1)%4, V(j) in V slot u%4. Issue K(j+3) and V(j+2) (their slots
     // were last read two steps ago); then
     //   region A: S(j+1) = QK(j+1) MFMAs interleaved with tile j's weights,
     //   check tile j's weights (rare path: raise m),
-    //   region B: O += P(j) V(j) MFMAs interleaved with the shift of S(j+1),
+    //   region B: O += P(j) V(j) MFMAs,
     // then mask tile j+1 if it is a diagonal tile.
     auto step = [&](auto slot_tag, int u, f32x16& scur, f32x16& snext) {
       constexpr int sl = decltype(slot_tag)::value;  // u % 4
@@ -517,35 +533,31 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
           u32x4 kf[KS];
 #pragma unroll
           for (int ks = 0; ks < 3 && ks < KS; ++ks) kf[ks] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ (ks << 5)));
-          snext = f32x16{};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             if (ks + 3 < KS) kf[ks + 3] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ ((ks + 3) << 5)));
-            snext = mfma32(kf[ks], qf[ks], snext);
+            snext = mfma32(kf[ks], qf[ks], ks == 0 ? negm : snext);
 #pragma unroll
             for (int pp = ks * NPAIR / KS; pp < (ks + 1) * NPAIR / KS; ++pp) {
               const int v = pp >> 2, w = pp & 3;
               const float p0 = __builtin_amdgcn_exp2f(scur[8 * v + 2 * w]);
               const float p1 = __builtin_amdgcn_exp2f(scur[8 * v + 2 * w + 1]);
-              const uint32_t pk = pack2(p0, p1);
-              pf[v][w] = pk;
-              if (w & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l1, false);
-              else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l0, false);
+              pf[v][w] = pack2(p0, p1);
+              l0 += p0;
+              l1 += p1;
             }
             __builtin_amdgcn_sched_barrier(0);
           }
           ls = l0 + l1;
         }
-        check(scur, pf, ls);
+        check(scur, pf, ls, &snext);
         __builtin_amdgcn_sched_barrier(0);
-        // region B (with the shift of tile j+1's scores)
+        // region B
         pv(std::integral_constant<int, sl>{}, pf);
-        shift(snext);
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);  // LDS read
 #pragma unroll
         for (int i = 0; i < 2 * DB; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 16 / (2 * DB), 1);  // VALU
           if (i + 3 < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -561,7 +573,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     auto last = [&](f32x16& scur) {
       if (!wave_rows) return;
       weights(scur, pf, ls);
-      check(scur, pf, ls);
+      check(scur, pf, ls, nullptr);
       pv(std::integral_constant<int, 0>{}, pf);
     };
     // The step count is rounded up so that the 4-way unrolled loop needs no remainder:

@@ -251,8 +251,10 @@ int extattn_kv_append(const void* k_new, const void* v_new, void* k_cache, void*
  * lse:          device [sum(E), Hq] float, or NULL to skip.
  * workspace:    device, at least the extattn_workspace_bytes() result, 256-byte
  *               aligned; its first 4 bytes hold the error word after the call.
- * Accumulation is fp32 for both element types; bf16 scores' softmax weights
- * are rounded to bf16 before the P.V product.
+ * Accumulation is fp32 for both element types. For bf16, the query rows of
+ * chunk tiles are multiplied by scale * log2(e) and rounded to bf16 before the
+ * Q.K product, and the softmax weights are rounded to bf16 before the P.V
+ * product.
  * Errors: EXTATTN_EINVAL for null required pointers, num_seqs < 1, any
  * extend < 1 or prefix < 0, Hq % Hkv != 0, a request needing more than
  * max_blocks blocks, a non-finite or non-positive scale, sum(E) above 2^31-1;
