@@ -482,8 +482,8 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     f32x16 sa, sb;
-    u32x4 pf[2];
-    float ls;
+    u32x4 pa[2], pb[2];  // packed weights of the tiles whose scores are in sa / sb
+    float la = 0.f, lb = 0.f;  // and this lane's sums of them
     // The first tile sets m to the rows' exact max (0 for rows with no visible key).
     if (wave_rows) {
       qk(std::integral_constant<int, 0>{}, sa);
@@ -496,15 +496,16 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
         sa[i] -= m;
         negm[i] = -m;
       }
+      weights(sa, pa, la);
     }
-    // Steady step u (tile j = t0 + u, not the last): S(j) is in scur (masked), K(j+1)
-    // in K slot (u+1)%4, V(j) in V slot u%4. Issue K(j+3) and V(j+2) (their slots
-    // were last read two steps ago); then
-    //   region A: S(j+1) = QK(j+1) MFMAs interleaved with tile j's weights,
-    //   check tile j's weights (rare path: raise m),
-    //   region B: O += P(j) V(j) MFMAs,
-    // then mask tile j+1 if it is a diagonal tile.
-    auto step = [&](auto slot_tag, int u, f32x16& scur, f32x16& snext) {
+    // Steady step u (tile j = t0 + u, not the last): S(j) is in scur (masked) and its
+    // weights in pcur / lcur, K(j+1) in K slot (u+1)%4, V(j) in V slot u%4. Issue
+    // K(j+3) and V(j+2) (their slots were last read two steps ago); then
+    //   region A: S(j+1) = QK(j+1) MFMAs,
+    //   check tile j's weights (rare path: raise m), mask tile j+1 if diagonal,
+    //   region B: O += P(j) V(j) MFMAs interleaved with tile j+1's weights.
+    auto step = [&](auto slot_tag, int u, f32x16& scur, f32x16& snext, u32x4 (&pcur)[2], u32x4 (&pnext)[2],
+                    float& lcur, float& lnext) {
       constexpr int sl = decltype(slot_tag)::value;  // u % 4
       const int j = t0 + u;
       // ids of tiles j+32 .. j+63 replace those of tiles j-32 .. j-1 (long consumed);
@@ -522,14 +523,10 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       pending = bk;
       if (wave_rows) {
         __builtin_amdgcn_sched_barrier(0);  // regions A and B are scheduled separately
-        // region A: the K operand reads run 3 ahead of their MFMAs, and each MFMA has
-        // one pair of tile j's weights next to it (fences keep that order)
+        // region A: the K operand reads run 3 ahead of their MFMAs
         {
           constexpr int sl1 = (sl + 1) & 3;
           const unsigned char* kb = smem + KBUF + sl1 * KT_BYTES;
-          constexpr int NPAIR = 8;  // weight pairs per lane and tile
-          static_assert(NPAIR % KS == 0 || KS % NPAIR == 0, "pairs must spread evenly over the k-steps");
-          float l0 = 0.f, l1 = 0.f;
           u32x4 kf[KS];
 #pragma unroll
           for (int ks = 0; ks < 3 && ks < KS; ++ks) kf[ks] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ (ks << 5)));
@@ -537,31 +534,43 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
           for (int ks = 0; ks < KS; ++ks) {
             if (ks + 3 < KS) kf[ks + 3] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ ((ks + 3) << 5)));
             snext = mfma32(kf[ks], qf[ks], ks == 0 ? negm : snext);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        check(scur, pcur, lcur, &snext);
+        mask(j + 1, snext);
+        __builtin_amdgcn_sched_barrier(0);
+        // region B: the V operand reads run 3 ahead; each MFMA has NPAIR / (2 DB) pairs
+        // of tile j+1's weights next to it
+        {
+          const unsigned char* vb = smem + VBUF + sl * KT_BYTES + v_off;
+          auto vread = [&](int i) -> u32x4 {
+            return *reinterpret_cast<const u32x4*>(vb + (i & 1) * VSUB + (i >> 1) * 32 * (kBlockSize * 2));
+          };
+          constexpr int NPAIR = 8;
+          constexpr int NB = 2 * DB;
+          static_assert(NPAIR % NB == 0, "pairs must spread evenly over the products");
+          float l0 = 0.f, l1 = 0.f;
+          u32x4 vf[NB];
 #pragma unroll
-            for (int pp = ks * NPAIR / KS; pp < (ks + 1) * NPAIR / KS; ++pp) {
+          for (int i = 0; i < 3 && i < NB; ++i) vf[i] = vread(i);
+#pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            if (i + 3 < NB) vf[i + 3] = vread(i + 3);
+            o[i >> 1] = mfma32(vf[i], pcur[i & 1], o[i >> 1]);
+#pragma unroll
+            for (int pp = i * NPAIR / NB; pp < (i + 1) * NPAIR / NB; ++pp) {
               const int v = pp >> 2, w = pp & 3;
-              const float p0 = __builtin_amdgcn_exp2f(scur[8 * v + 2 * w]);
-              const float p1 = __builtin_amdgcn_exp2f(scur[8 * v + 2 * w + 1]);
-              pf[v][w] = pack2(p0, p1);
+              const float p0 = __builtin_amdgcn_exp2f(snext[8 * v + 2 * w]);
+              const float p1 = __builtin_amdgcn_exp2f(snext[8 * v + 2 * w + 1]);
+              pnext[v][w] = pack2(p0, p1);
               l0 += p0;
               l1 += p1;
             }
             __builtin_amdgcn_sched_barrier(0);
           }
-          ls = l0 + l1;
+          lnext = l0 + l1;
         }
-        check(scur, pf, ls, &snext);
-        __builtin_amdgcn_sched_barrier(0);
-        // region B
-        pv(std::integral_constant<int, sl>{}, pf);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);  // LDS read
-#pragma unroll
-        for (int i = 0; i < 2 * DB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-          if (i + 3 < 2 * DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        mask(j + 1, snext);
       }
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(kIssuePerStep) : "memory");
       if (j == j_clip) {  // V(j+1) has landed: clear its keys past the end
@@ -569,24 +578,23 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
     };
-    // The last tile: weights, check and P V with the sequence-end clip; nothing to issue.
-    auto last = [&](f32x16& scur) {
+    // The last tile: check and P V with the sequence-end clip; nothing to issue.
+    auto last = [&](f32x16& scur, u32x4 (&pcur)[2], float& lcur) {
       if (!wave_rows) return;
-      weights(scur, pf, ls);
-      check(scur, pf, ls, nullptr);
-      pv(std::integral_constant<int, 0>{}, pf);
+      check(scur, pcur, lcur, nullptr);
+      pv(std::integral_constant<int, 0>{}, pcur);
     };
     // The step count is rounded up so that the 4-way unrolled loop needs no remainder:
     // tiles past the range's end read the zero page and are masked out entirely.
     const int npad = n + ((1 - n) & 3);  // npad = 1 (mod 4), npad >= n
     for (int u = 0; u + 4 < npad; u += 4) {
-      step(std::integral_constant<int, 0>{}, u, sa, sb);
-      step(std::integral_constant<int, 1>{}, u + 1, sb, sa);
-      step(std::integral_constant<int, 2>{}, u + 2, sa, sb);
-      step(std::integral_constant<int, 3>{}, u + 3, sb, sa);
+      step(std::integral_constant<int, 0>{}, u, sa, sb, pa, pb, la, lb);
+      step(std::integral_constant<int, 1>{}, u + 1, sb, sa, pb, pa, lb, la);
+      step(std::integral_constant<int, 2>{}, u + 2, sa, sb, pa, pb, la, lb);
+      step(std::integral_constant<int, 3>{}, u + 3, sb, sa, pb, pa, lb, la);
     }
     // tile t0 + npad - 1 (npad - 1 is a multiple of 4): S in sa, V in ring slot 0
-    last(sa);
+    last(sa, pa, la);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads issued past the end
   }
   write_row<D>(a, o, m, l, valid, hi, orow, it.slot, it.slot_rows, rloc);
