@@ -551,7 +551,14 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
           constexpr int NB = 2 * DB;
           static_assert(NPAIR % NB == 0, "pairs must spread evenly over the products");
           float l0 = 0.f, l1 = 0.f;
+          float e[16];
           u32x4 vf[NB];
+          auto finish = [&](int pp) {  // pack and sum pair pp (its exps were issued one group earlier)
+            const int v = pp >> 2, w = pp & 3;
+            pnext[v][w] = pack2(e[2 * pp], e[2 * pp + 1]);
+            l0 += e[2 * pp];
+            l1 += e[2 * pp + 1];
+          };
 #pragma unroll
           for (int i = 0; i < 3 && i < NB; ++i) vf[i] = vread(i);
 #pragma unroll
@@ -561,14 +568,17 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
 #pragma unroll
             for (int pp = i * NPAIR / NB; pp < (i + 1) * NPAIR / NB; ++pp) {
               const int v = pp >> 2, w = pp & 3;
-              const float p0 = __builtin_amdgcn_exp2f(snext[8 * v + 2 * w]);
-              const float p1 = __builtin_amdgcn_exp2f(snext[8 * v + 2 * w + 1]);
-              pnext[v][w] = pack2(p0, p1);
-              l0 += p0;
-              l1 += p1;
+              e[2 * pp] = __builtin_amdgcn_exp2f(snext[8 * v + 2 * w]);
+              e[2 * pp + 1] = __builtin_amdgcn_exp2f(snext[8 * v + 2 * w + 1]);
+            }
+            if (i > 0) {
+#pragma unroll
+              for (int pp = (i - 1) * NPAIR / NB; pp < i * NPAIR / NB; ++pp) finish(pp);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
+#pragma unroll
+          for (int pp = (NB - 1) * NPAIR / NB; pp < NPAIR; ++pp) finish(pp);
           lnext = l0 + l1;
         }
       }
