@@ -556,9 +556,17 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
           auto finish = [&](int pp) {  // pack and sum pair pp (its exps were issued one group earlier)
             const int v = pp >> 2, w = pp & 3;
             pnext[v][w] = pack2(e[2 * pp], e[2 * pp + 1]);
-            l0 += e[2 * pp];
-            l1 += e[2 * pp + 1];
+            if (pp == 0) {
+              l0 = e[0];
+              l1 = e[1];
+            } else {
+              l0 += e[2 * pp];
+              l1 += e[2 * pp + 1];
+            }
           };
+          // exps of pairs [lo(i), lo(i+1)) go with MFMA i, front-loaded so that the last
+          // MFMA has none after it
+          auto lo = [](int i) { return i >= NB ? NPAIR : min(NPAIR, (i * NPAIR + NB - 2) / (NB - 1)); };
 #pragma unroll
           for (int i = 0; i < 3 && i < NB; ++i) vf[i] = vread(i);
 #pragma unroll
@@ -566,19 +574,19 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
             if (i + 3 < NB) vf[i + 3] = vread(i + 3);
             o[i >> 1] = mfma32(vf[i], pcur[i & 1], o[i >> 1]);
 #pragma unroll
-            for (int pp = i * NPAIR / NB; pp < (i + 1) * NPAIR / NB; ++pp) {
+            for (int pp = lo(i); pp < lo(i + 1); ++pp) {
               const int v = pp >> 2, w = pp & 3;
               e[2 * pp] = __builtin_amdgcn_exp2f(snext[8 * v + 2 * w]);
               e[2 * pp + 1] = __builtin_amdgcn_exp2f(snext[8 * v + 2 * w + 1]);
             }
             if (i > 0) {
 #pragma unroll
-              for (int pp = (i - 1) * NPAIR / NB; pp < i * NPAIR / NB; ++pp) finish(pp);
+              for (int pp = lo(i - 1); pp < lo(i); ++pp) finish(pp);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
 #pragma unroll
-          for (int pp = (NB - 1) * NPAIR / NB; pp < NPAIR; ++pp) finish(pp);
+          for (int pp = lo(NB - 1); pp < lo(NB); ++pp) finish(pp);
           lnext = l0 + l1;
         }
       }
