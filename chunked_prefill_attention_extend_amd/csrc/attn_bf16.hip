@@ -499,9 +499,9 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       weights(sa, pa, la);
     }
     // Steady step u (tile j = t0 + u, not the last): S(j) is in scur (masked) and its
-    // weights in pcur / lcur, K(j+1) in K slot (u+1)%4, V(j) in V slot u%4. Issue
-    // K(j+3) and V(j+2) (their slots were last read two steps ago); then
-    //   region A: S(j+1) = QK(j+1) MFMAs,
+    // weights in pcur / lcur, K(j+1) in K slot (u+1)%4, V(j) in V slot u%4. Then
+    //   region A: S(j+1) = QK(j+1) MFMAs, with the copies of K(j+3) and V(j+2) (their
+    //     slots were last read two steps ago) issued half way,
     //   check tile j's weights (rare path: raise m), mask tile j+1 if diagonal,
     //   region B: O += P(j) V(j) MFMAs interleaved with tile j+1's weights.
     auto step = [&](auto slot_tag, int u, f32x16& scur, f32x16& snext, u32x4 (&pcur)[2], u32x4 (&pnext)[2],
@@ -517,10 +517,16 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       if constexpr (sl == 1) {
         if (((u + 3) & 31) == 0) load_window((u + 3) >> 5);  // tile j+3 starts a new window
       }
-      const int32_t bk = read_blk(j + 3);
-      issue_k(bk, (sl + 3) & 3);
-      issue_v(pending, (sl + 2) & 3);
-      pending = bk;
+      // This step's tile copies (K(j+3), V(j+2); their slots are not read in this step)
+      // go out in the middle of region A, after the first QK MFMAs are under way;
+      // waves without rows issue them at once.
+      auto issue = [&]() {
+        const int32_t bk = read_blk(j + 3);
+        issue_k(bk, (sl + 3) & 3);
+        issue_v(pending, (sl + 2) & 3);
+        pending = bk;
+      };
+      if (!wave_rows) issue();
       if (wave_rows) {
         __builtin_amdgcn_sched_barrier(0);  // regions A and B are scheduled separately
         // region A: the K operand reads run 3 ahead of their MFMAs
@@ -534,6 +540,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
           for (int ks = 0; ks < KS; ++ks) {
             if (ks + 3 < KS) kf[ks + 3] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ ((ks + 3) << 5)));
             snext = mfma32(kf[ks], qf[ks], ks == 0 ? negm : snext);
+            if (ks == KS / 2 - 1) issue();
             __builtin_amdgcn_sched_barrier(0);
           }
         }
