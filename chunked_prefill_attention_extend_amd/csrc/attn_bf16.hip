@@ -402,9 +402,9 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   };
   // Check of a tile's weights before they enter P.V: when some lane's sum passed
   // kSumBound (or overflowed), raise m by the rows' exact max over the (shifted)
-  // tile, rescale O and l, shift the tile and the next one (already computed from
-  // the old m) again and redo the tile's weights. Then add the sum to l.
-  auto check = [&](f32x16& s, u32x4 (&pf)[2], float& ls, f32x16* snext) {
+  // tile, rescale O and l, shift the tile again and redo its weights (the next
+  // tile's products start from the new m). Then add the sum to l.
+  auto check = [&](f32x16& s, u32x4 (&pf)[2], float& ls) {
     if (__builtin_amdgcn_ballot_w64(ls > kSumBound) != 0) {
       float mx = row_max(s);
       mx = fmaxf(mx, partner(mx, hi));
@@ -416,10 +416,6 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       m += d;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] -= d;
-      if (snext) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) (*snext)[i] -= d;
-      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) negm[i] = -m;
       weights(s, pf, ls);
@@ -500,9 +496,10 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     }
     // Steady step u (tile j = t0 + u, not the last): S(j) is in scur (masked) and its
     // weights in pcur / lcur, K(j+1) in K slot (u+1)%4, V(j) in V slot u%4. Then
+    //   check tile j's weights (rare path: raise m before the next products),
     //   region A: S(j+1) = QK(j+1) MFMAs, with the copies of K(j+3) and V(j+2) (their
     //     slots were last read two steps ago) issued half way,
-    //   check tile j's weights (rare path: raise m), mask tile j+1 if diagonal,
+    //   mask tile j+1 if diagonal,
     //   region B: O += P(j) V(j) MFMAs interleaved with tile j+1's weights.
     auto step = [&](auto slot_tag, int u, f32x16& scur, f32x16& snext, u32x4 (&pcur)[2], u32x4 (&pnext)[2],
                     float& lcur, float& lnext) {
@@ -528,6 +525,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       };
       if (!wave_rows) issue();
       if (wave_rows) {
+        check(scur, pcur, lcur);
         __builtin_amdgcn_sched_barrier(0);  // regions A and B are scheduled separately
         // region A: the K operand reads run 3 ahead of their MFMAs
         {
@@ -544,7 +542,6 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        check(scur, pcur, lcur, &snext);
         mask(j + 1, snext);
         __builtin_amdgcn_sched_barrier(0);
         // region B: the V operand reads run 3 ahead; each MFMA has NPAIR / (2 DB) pairs
@@ -606,7 +603,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     // The last tile: check and P V with the sequence-end clip; nothing to issue.
     auto last = [&](f32x16& scur, u32x4 (&pcur)[2], float& lcur) {
       if (!wave_rows) return;
-      check(scur, pcur, lcur, nullptr);
+      check(scur, pcur, lcur);
       pv(std::integral_constant<int, 0>{}, pcur);
     };
     // The step count is rounded up so that the 4-way unrolled loop needs no remainder:
