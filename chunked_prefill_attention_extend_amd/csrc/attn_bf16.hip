@@ -371,7 +371,8 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   // Causal mask of a diagonal tile (and of keys past the range end). Element i holds
   // key kt + 8 hi + key_of_elem(i, 0), so the test is one threshold against constants.
   // first tile index whose last key passes lim_min (tiles from there on may need masking)
-  const int j_mask = lim_min >= KT - 1 ? (lim_min - (KT - 1)) / KT + 1 : 0;
+  const int j_mask =
+      __builtin_amdgcn_readfirstlane(lim_min >= KT - 1 ? (lim_min - (KT - 1)) / KT + 1 : 0);  // uniform
   auto mask = [&](int j, f32x16& s) {
     const int kt = j * KT;
     if (j >= j_mask) {
