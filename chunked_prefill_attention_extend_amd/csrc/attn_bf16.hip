@@ -385,7 +385,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   // Scores leave their QK product shifted, s c - m (log2 units): Q carries the scale
   // and the product starts from -m. Weights p = 2^s as packed bf16 for the P.V
   // product, and this lane's fp32 sum of them over the tile, taken before the
-  // rounding (lse stays exact up to fp32 arithmetic; the normaliser is within 2^-9
+  // rounding (lse carries no rounding of the weights; the normaliser is within 2^-9
   // relative of the rounded weights' sum).
   auto weights = [&](const f32x16& s, u32x4 (&pf)[2], float& ls) {
     float l0 = 0.f, l1 = 0.f;
@@ -545,8 +545,8 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
         }
         mask(j + 1, snext);
         __builtin_amdgcn_sched_barrier(0);
-        // region B: the V operand reads run 3 ahead; each MFMA has NPAIR / (2 DB) pairs
-        // of tile j+1's weights next to it
+        // region B: the V operand reads run 3 ahead; tile j+1's weights go next to the
+        // MFMAs (exps front-loaded, each pair packed and summed one MFMA later)
         {
           const unsigned char* vb = smem + VBUF + sl * KT_BYTES + v_off;
           auto vread = [&](int i) -> u32x4 {
@@ -554,7 +554,6 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
           };
           constexpr int NPAIR = 8;
           constexpr int NB = 2 * DB;
-          static_assert(NPAIR % NB == 0, "pairs must spread evenly over the products");
           float l0 = 0.f, l1 = 0.f;
           float e[16];
           u32x4 vf[NB];
