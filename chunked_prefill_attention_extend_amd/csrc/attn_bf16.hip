@@ -545,12 +545,13 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
         }
         mask(j + 1, snext);
         __builtin_amdgcn_sched_barrier(0);
-        // region B: the V operand reads run 3 ahead; tile j+1's weights go next to the
-        // MFMAs (exps front-loaded, each pair packed and summed one MFMA later)
+        // region B: the V operand reads run 3 ahead; consecutive MFMAs update different
+        // O blocks (16-key half b = i / DB, feature block i % DB); tile j+1's weights go
+        // next to the MFMAs (exps front-loaded, each pair packed and summed one MFMA later)
         {
           const unsigned char* vb = smem + VBUF + sl * KT_BYTES + v_off;
           auto vread = [&](int i) -> u32x4 {
-            return *reinterpret_cast<const u32x4*>(vb + (i & 1) * VSUB + (i >> 1) * 32 * (kBlockSize * 2));
+            return *reinterpret_cast<const u32x4*>(vb + (i / DB) * VSUB + (i % DB) * 32 * (kBlockSize * 2));
           };
           constexpr int NPAIR = 8;
           constexpr int NB = 2 * DB;
@@ -576,7 +577,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
 #pragma unroll
           for (int i = 0; i < NB; ++i) {
             if (i + 3 < NB) vf[i + 3] = vread(i + 3);
-            o[i >> 1] = mfma32(vf[i], pcur[i & 1], o[i >> 1]);
+            o[i % DB] = mfma32(vf[i], pcur[i / DB], o[i % DB]);
 #pragma unroll
             for (int pp = lo(i); pp < lo(i + 1); ++pp) {
               const int v = pp >> 2, w = pp & 3;
