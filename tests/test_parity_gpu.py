@@ -208,6 +208,27 @@ def test_kv_append_layout():
         assert np.array_equal(vc[b, :, :, s], v[p]), f"V of token {p}"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kv_append_layout_whole_blocks(dtype):
+    """Appends that start on a block boundary fill whole cache blocks (the kernel's
+    wide-row V path), followed by a ragged tail: every token lands where the block
+    table says, in both element types."""
+    w = custom_workload(43, [(16, 53)], 8, 2, 128, dtype=dtype, mult=0.5 if dtype == "bf16" else 1.0,
+                        permute=True)
+    r = w.requests[0]
+    cache = PagedCache(w, fill=0.0)
+    k = w.k(r, 0, 69)
+    v = w.v(r, 0, 69)
+    cache.append([0], [0], k[:16], v[:16], [16])      # one whole block
+    cache.append([0], [16], k[16:], v[16:], [53])     # three whole blocks and a 5-token tail
+    kc = cache.k.float().cpu().numpy()
+    vc = cache.v.float().cpu().numpy()
+    for p in range(69):
+        b, s = r.blocks[p // 16], p % 16
+        assert np.array_equal(kc[b, :, s, :], k[p]), f"K of token {p}"
+        assert np.array_equal(vc[b, :, :, s], v[p]), f"V of token {p}"
+
+
 def test_invalid_block_ids_are_counted_not_read():
     w = custom_workload(51, [(40, 8)], 8, 8, 128)
     cache = PagedCache(w, fill=0.0)
