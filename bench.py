@@ -544,7 +544,7 @@ def main() -> int:
                     help="only measure verify rows (E = 1..8 query rows per request) in HBM GB/s")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        print("bench.py runs on one GPU: the library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         return 2
 
     import torch
