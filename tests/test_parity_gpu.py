@@ -120,6 +120,28 @@ def test_many_decode_rows():
     check_launch(sub, out, lse, q_off, q, what="many decode rows")
 
 
+@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5, 6])
+def test_random_mixed_launches(seed):
+    """Random launches: head layout, head_dim, and a mix of decode rows, verify rows,
+    short and long chunks with random prefixes (ragged against blocks and tiles),
+    compared with the oracle on up to 24 sampled rows per request."""
+    rng = np.random.default_rng(1000 + seed)
+    hq, hkv = [(32, 8), (64, 8), (16, 16), (28, 4), (8, 1)][seed % 5]
+    d = 128 if seed % 3 else 64
+    launches = []
+    for _ in range(int(rng.integers(2, 9))):
+        kind = int(rng.integers(0, 4))
+        p = int(rng.integers(0, 6000))
+        e = {0: 1, 1: int(rng.integers(2, 9)), 2: int(rng.integers(9, 300)), 3: int(rng.integers(300, 1500))}[kind]
+        launches.append((p, e))
+    w = custom_workload(5000 + seed, launches, hq, hkv, d)
+    log(f"random launch {seed}: {launches} Hq={hq} Hkv={hkv} D={d}")
+    out, lse, q_off, q = run_launch(w)
+    sample = {r.index: np.unique(np.concatenate([[0, r.launch[1] - 1], rng.integers(0, r.launch[1], 22)]))
+              for r in w.requests}
+    check_launch(w, out, lse, q_off, q, row_sample=sample, what=f"random launch {seed}")
+
+
 def test_timed_variant_same_results_and_sane_stamps():
     """The measurement variant gives bit-identical results and one
     {start, end, kind, request} record per work item."""
