@@ -111,3 +111,23 @@ def test_fused_append_invalid_block_ids_are_counted_not_written():
     assert not torch.equal(fus.k[blocks[2]], before[blocks[2]])
     others = [b for b in range(w.num_blocks) if b != blocks[2]]
     assert torch.equal(fus.k[others], before[others])
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_fused_append_random_launches(seed):
+    """Random mixed launches through the fused path: caches, out and lse bit for bit
+    as kv_append followed by extend_attention."""
+    rng = np.random.default_rng(2000 + seed)
+    hq, hkv, d = [(32, 8, 128), (64, 8, 128), (16, 4, 64)][seed % 3]
+    launches = []
+    for _ in range(int(rng.integers(2, 7))):
+        kind = int(rng.integers(0, 3))
+        p = int(rng.integers(0, 5000))
+        e = {0: 1, 1: int(rng.integers(2, 9)), 2: int(rng.integers(9, 900))}[kind]
+        launches.append((p, e))
+    w = custom_workload(3000 + seed, launches, hq, hkv, d)
+    log(f"fused append, random launch {seed}: {launches} Hq={hq} Hkv={hkv} D={d}")
+    (o1, l1, sep), (o2, l2, fus), err, q = _run_both(w)
+    assert err == 0, f"error word {err:#x}"
+    assert torch.equal(_bits(sep.k), _bits(fus.k)) and torch.equal(_bits(sep.v), _bits(fus.v))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
