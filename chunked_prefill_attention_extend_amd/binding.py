@@ -273,10 +273,19 @@ def _check_cache(k_cache, v_cache, block_table):
     return nb, hkv, bs, d
 
 
-def _workspace(nbytes: int, device, workspace):
+def _workspace(nbytes: int, device, workspace, stream=None):
+    """The caller's workspace, or a new one. A new one must stay referenced until
+    every launch that uses it has been enqueued: once freed, torch's caching
+    allocator may hand its memory to the next allocation (it did to the stamp
+    buffer of a timed launch, whose stamps then overwrote the zero page). On a
+    stream other than torch's current one it is also marked as in use there, so
+    that the allocator waits for that stream's work before reusing it."""
     import torch
     if workspace is None:
-        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        if stream is not None:
+            ws.record_stream(stream)
+        return ws
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError("workspace too small")
     return workspace
@@ -295,7 +304,7 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, prefix_lens, extend_l
         if tuple(t.shape) != (total, hkv, d) or t.dtype != k_cache.dtype or not t.is_contiguous() or not t.is_cuda:
             raise ValueError("k_new / v_new must be contiguous device tensors [sum(E), Hkv, D] of the cache dtype")
     need = lib.extattn_kv_append_workspace_bytes(len(p))
-    ws = _workspace(need, k_cache.device, workspace)
+    ws = _workspace(need, k_cache.device, workspace, stream)
     _check(lib.extattn_kv_append(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                  block_table.data_ptr(), block_table.shape[1], nb, _ptr(p), _ptr(e), len(p),
                                  hkv, d, bs, _dtype_code(k_cache), ws.data_ptr(),
@@ -303,7 +312,8 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, prefix_lens, extend_l
 
 
 def _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale, out, lse, workspace, stream):
-    """Checks shared by the extend-attention entry points; returns (lib, p, e, hkv, d, args)."""
+    """Checks shared by the extend-attention entry points; returns (lib, p, e, hkv, d, ws, args).
+    The caller holds ``ws`` (the workspace, maybe allocated here) until its launches are enqueued."""
     import torch
     lib = load_library()
     nb, hkv, bs, d = _check_cache(k_cache, v_cache, block_table)
@@ -323,7 +333,7 @@ def _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, sca
         raise ValueError("lse must be a contiguous float32 [sum(E), Hq] tensor")
     code = _dtype_code(q)
     if workspace is None:
-        ws = _workspace(workspace_bytes(p, e, hq, hkv, d, code), q.device, None)
+        ws = _workspace(workspace_bytes(p, e, hq, hkv, d, code), q.device, None, stream)
     else:  # the library checks the size itself (EXTATTN_ENOSPC): no second planning pass here
         if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or not workspace.is_cuda:
             raise ValueError("workspace must be a contiguous uint8 device tensor")
@@ -332,7 +342,7 @@ def _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, sca
             _ptr(p), _ptr(e), len(p), hq, hkv, d, bs, float(scale), code, out.data_ptr(),
             lse.data_ptr() if lse is not None else None, ws.data_ptr(), ws.numel() * ws.element_size(),
             _stream_handle(stream))
-    return lib, p, e, hkv, d, args
+    return lib, p, e, hkv, d, ws, args
 
 
 def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale: float, out,
@@ -346,8 +356,8 @@ def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens,
     of {start, end, kind (0 chunk, 1 decode / verify), request} per work item.
     """
     import torch
-    lib, _, _, _, _, args = _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale, out,
-                                         lse, workspace, stream)
+    lib, p, e, _, _, ws, args = _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale,
+                                             out, lse, workspace, stream)
     if not timed:
         _check(lib.extattn_extend_attention(*args))
         return out
@@ -359,6 +369,7 @@ def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens,
         raise RuntimeError("timed launch: no work items")
     stamps = torch.empty((n.value, 4), dtype=torch.int64, device=q.device)
     _check(lib.extattn_extend_attention_timed(*args, stamps.data_ptr(), n.value, ctypes.byref(n), ctypes.byref(hz)))
+    del ws, p, e  # enqueued: stream order now protects the workspace
     return out, stamps, hz.value
 
 
@@ -367,8 +378,8 @@ def extend_attention_append(q, k_new, v_new, k_cache, v_cache, block_table, pref
     """KV append fused into the extend launch: writes k_new / v_new (device
     ``[sum(E), Hkv, D]``) into the paged cache at positions prefix + t and computes
     the same attention as ``extend_attention``, in one attention launch. Returns ``out``."""
-    lib, p, e, hkv, d, args = _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale, out,
-                                           lse, workspace, stream)
+    lib, p, e, hkv, d, ws, args = _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale,
+                                               out, lse, workspace, stream)
     total = int(e.sum())
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if tuple(t.shape) != (total, hkv, d) or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:

@@ -177,6 +177,51 @@ def test_timed_variant_same_results_and_sane_stamps():
     assert (st[:, 1].max() - st[:, 0].min()) / hz < 1.0
 
 
+def test_timed_launch_holds_its_workspace(monkeypatch):
+    """A timed launch without a caller workspace keeps the workspace that the
+    binding allocates referenced until both of its library calls have been made,
+    so the stamp buffer allocated between them never takes that memory (stamps
+    written over the workspace's zero page reach the values of padded key tiles)."""
+    import weakref
+    from chunked_prefill_attention_extend_amd import binding
+    made = []
+    real_ws = binding._workspace
+
+    def spy(*args, **kw):
+        t = real_ws(*args, **kw)
+        made.append(weakref.ref(t))
+        return t
+
+    lib = binding.load_library()
+    real_timed = lib.extattn_extend_attention_timed
+    seen = []
+
+    def timed(*args):  # args: the 20 launch arguments, then stamps, capacity, n_items, tick_hz
+        seen.append((args[17], args[18], args[20], [r() is not None for r in made]))
+        return real_timed(*args)
+
+    monkeypatch.setattr(binding, "_workspace", spy)
+    monkeypatch.setattr(lib, "extattn_extend_attention_timed", timed)
+    launches = [(3000, 1), (900, 600), (12, 1)]
+    w = custom_workload(62, launches, 32, 8, 128)
+    log("timed variant: workspace lifetime")
+    cache = PagedCache(w)
+    for r in w.requests:
+        p, e = r.launch
+        cache.append([r.index], [0], w.k(r, 0, p + e), w.v(r, 0, p + e), [p + e])
+    q = dev_tensor(np.concatenate([w.q(r, p, p + e) for r, (p, e) in zip(w.requests, launches)]), w.dtype)
+    o = torch.empty_like(q)
+    made.clear()  # the cache appends above allocated their own
+    _, stamps, _ = ext.extend_attention(q, cache.k, cache.v, cache.bt, [p for p, _ in launches],
+                                        [e for _, e in launches], w.scale, o, None, timed=True)
+    torch.cuda.synchronize()
+    assert len(made) == 1 and len(seen) == 2, (len(made), len(seen))
+    assert all(all(alive) for *_, alive in seen), "the workspace was freed before the launch"
+    ws_ptr, ws_bytes, st_ptr, _ = seen[1]
+    st_bytes = stamps.numel() * stamps.element_size()
+    assert st_ptr + st_bytes <= ws_ptr or st_ptr >= ws_ptr + ws_bytes, "stamps overlap the workspace"
+
+
 def test_fp32_mixed_and_gqa():
     w = custom_workload(7, [(50, 30), (129, 1), (0, 70)], 8, 2, 128, dtype="f32", mult=1.0)
     log("fp32 mixed launch with GQA")
