@@ -109,7 +109,7 @@ def sweep_step(ext, s, events=None, fused=False):
                 events[t][0].record()
             ext.extend_attention_append(s["q"][p:p + e], s["k_new"][p:p + e], s["v_new"][p:p + e], s["k_cache"],
                                         s["v_cache"], s["bt"], [p], [e], s["scale"], s["out"][p:p + e],
-                                        s["lse"][p:p + e], workspace=s["ws"])
+                                        s["lse"][p:p + e], workspace=s["ws"], check=False)
             if events is not None:
                 events[t][1].record()
             continue
@@ -121,6 +121,17 @@ def sweep_step(ext, s, events=None, fused=False):
                              s["out"][p:p + e], s["lse"][p:p + e], workspace=s["ws"])
         if events is not None:
             events[t][1].record()
+
+
+def check_status(ext, s) -> None:
+    """Raise if the last launches left a status flag in their workspaces (an
+    invalid block id, a fused-append wait that gave up): their timings would not
+    stand for valid results."""
+    for name, ws in (("attention", s["ws"]), ("kv_append", s["kv_ws"])):
+        flags, count, exact = ext.read_status(ws)
+        err = ext.status_error(flags, count, name)
+        if err is not None:
+            raise err
 
 
 def mixed_step_bench(torch, ext, synth, reps: int = 10):
@@ -597,6 +608,7 @@ def main() -> int:
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {dt:.3f} s")
+    check_status(ext, s)
     kern_s = sum(a.elapsed_time(b) for step in events for a, b in step) * 1e-3 / args.steps
     per_launch_s = kern_s / nchunk
     achieved = flops / nchunk / per_launch_s / 1e12
@@ -620,6 +632,7 @@ def main() -> int:
             sweep_step(ext, s, fused=True)
         torch.cuda.synchronize()
         dtf = time.perf_counter() - t0
+        check_status(ext, s)
         fused = {"ms_per_step": dtf / args.steps * 1e3, "tflops": flops / (dtf / args.steps) / 1e12,
                  "note": "128 x extend_attention_append (append inside the attention launch)"}
         log(f"fused steps: {dtf / args.steps * 1e3:.1f} ms per step")

@@ -9,16 +9,21 @@ from .binding import (  # noqa: F401
     EXTATTN_BF16,
     EXTATTN_F32,
     LIB_PATH,
+    STATUS_BAD_BLOCK,
+    STATUS_WAIT_TIMEOUT,
     chunk_plan,
     decode_first_with_slack,
     extend_attention,
     extend_attention_append,
     kv_append,
+    last_status,
     load_library,
     mixed_chunk_step,
     plan_cache_clear,
     plan_cache_configure,
     plan_cache_stats,
+    read_status,
+    status_error,
     token_budget_step,
     workspace_bytes,
 )

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libextattn.so")
 
 EXTATTN_OK, EXTATTN_EINVAL, EXTATTN_ENOSPC, EXTATTN_EUNSUPPORTED, EXTATTN_EHIP = 0, -1, -2, -3, -4
 EXTATTN_BF16, EXTATTN_F32 = 0, 1
+STATUS_BAD_BLOCK, STATUS_WAIT_TIMEOUT = 1, 2
 BLOCK_SIZE = 16
 
 _lib = None
@@ -82,6 +83,9 @@ def load_library() -> ctypes.CDLL:
     lib.extattn_plan_cache_stats.argtypes = [_c_i64p, _c_i64p, _c_i32p, _c_i64p]
     lib.extattn_plan_cache_clear.restype = ctypes.c_int
     lib.extattn_plan_cache_clear.argtypes = []
+    lib.extattn_read_status.restype = ctypes.c_int
+    lib.extattn_read_status.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32), _c_i32p, _c_i32p,
+                                        ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -95,6 +99,45 @@ def _check(rc: int) -> None:
     kind = {EXTATTN_EINVAL: "invalid argument", EXTATTN_ENOSPC: "insufficient space",
             EXTATTN_EUNSUPPORTED: "unsupported"}.get(rc, f"status {rc}")
     raise ValueError(f"extattn {kind}: {msg}")
+
+
+def status_error(flags: int, bad_block_reads: int, what: str = "launch"):
+    """The exception that a non-zero status stands for, or None."""
+    if flags & STATUS_WAIT_TIMEOUT:
+        return RuntimeError(f"extattn {what}: a fused-append wait gave up; the results are not valid")
+    if flags & STATUS_BAD_BLOCK:
+        return ValueError(f"extattn {what}: {bad_block_reads} read(s) of a block id outside [0, num_blocks); "
+                          "the results are not valid")
+    if flags:
+        return RuntimeError(f"extattn {what}: unknown status flags {flags:#x}")
+    return None
+
+
+_last_status = (0, 0, 0)
+
+
+def read_status(workspace, stream=None) -> tuple[int, int, int]:
+    """``(flags, bad_block_reads, exact_waves)`` left in ``workspace`` by the last
+    call that used it (waits for ``stream``, default torch's current stream)."""
+    global _last_status
+    flags, count, exact = ctypes.c_uint32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load_library().extattn_read_status(workspace.data_ptr(), ctypes.byref(flags), ctypes.byref(count),
+                                              ctypes.byref(exact), _stream_handle(stream)))
+    _last_status = (flags.value, count.value, exact.value)
+    return _last_status
+
+
+def last_status() -> tuple[int, int, int]:
+    """The status words of the most recent ``read_status`` (also the one a
+    ``check=True`` call makes)."""
+    return _last_status
+
+
+def _raise_on_status(ws, stream, what: str) -> None:
+    flags, count, _ = read_status(ws, stream)
+    err = status_error(flags, count, what)
+    if err is not None:
+        raise err
 
 
 def _host_i32(x: Sequence[int]) -> np.ndarray:
@@ -292,8 +335,10 @@ def _workspace(nbytes: int, device, workspace, stream=None):
 
 
 def kv_append(k_new, v_new, k_cache, v_cache, block_table, prefix_lens, extend_lens,
-              workspace=None, stream=None) -> None:
-    """Write each request's new K/V rows ``[sum(E), Hkv, D]`` into the paged cache."""
+              workspace=None, stream=None, check: bool = False) -> None:
+    """Write each request's new K/V rows ``[sum(E), Hkv, D]`` into the paged cache.
+    With ``check`` the call waits for the stream and raises if a block id was
+    outside ``[0, num_blocks)``."""
     lib = load_library()
     nb, hkv, bs, d = _check_cache(k_cache, v_cache, block_table)
     p, e = _host_i32(prefix_lens), _host_i32(extend_lens)
@@ -309,6 +354,8 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, prefix_lens, extend_l
                                  block_table.data_ptr(), block_table.shape[1], nb, _ptr(p), _ptr(e), len(p),
                                  hkv, d, bs, _dtype_code(k_cache), ws.data_ptr(),
                                  ws.numel() * ws.element_size(), _stream_handle(stream)))
+    if check:
+        _raise_on_status(ws, stream, "kv_append")
 
 
 def _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale, out, lse, workspace, stream):
@@ -346,7 +393,7 @@ def _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, sca
 
 
 def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale: float, out,
-                     lse=None, workspace=None, stream=None, timed: bool = False):
+                     lse=None, workspace=None, stream=None, timed: bool = False, check: bool = False):
     """Chunked-prefill extend attention over the paged cache.
 
     q, out: device ``[sum(E), Hq, D]``; lse: device float32 ``[sum(E), Hq]`` or None;
@@ -354,12 +401,18 @@ def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens,
     Returns ``out``; with ``timed`` (bf16 only) the measurement variant runs and
     ``(out, stamps, tick_hz)`` is returned, ``stamps`` a device int64 ``[items, 4]``
     of {start, end, kind (0 chunk, 1 decode / verify), request} per work item.
+    With ``check`` the call waits for the stream and raises if the launch met a
+    block id outside ``[0, num_blocks)`` (``ValueError``). Without it the status
+    stays in the workspace (``read_status``); a workspace allocated here is
+    dropped with it.
     """
     import torch
     lib, p, e, _, _, ws, args = _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale,
                                              out, lse, workspace, stream)
     if not timed:
         _check(lib.extattn_extend_attention(*args))
+        if check:
+            _raise_on_status(ws, stream, "extend_attention")
         return out
     n = ctypes.c_int32(0)
     hz = ctypes.c_double(0.0)
@@ -369,15 +422,23 @@ def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens,
         raise RuntimeError("timed launch: no work items")
     stamps = torch.empty((n.value, 4), dtype=torch.int64, device=q.device)
     _check(lib.extattn_extend_attention_timed(*args, stamps.data_ptr(), n.value, ctypes.byref(n), ctypes.byref(hz)))
+    if check:
+        _raise_on_status(ws, stream, "extend_attention (timed)")
     del ws, p, e  # enqueued: stream order now protects the workspace
     return out, stamps, hz.value
 
 
 def extend_attention_append(q, k_new, v_new, k_cache, v_cache, block_table, prefix_lens, extend_lens,
-                            scale: float, out, lse=None, workspace=None, stream=None):
+                            scale: float, out, lse=None, workspace=None, stream=None, check: bool = True):
     """KV append fused into the extend launch: writes k_new / v_new (device
     ``[sum(E), Hkv, D]``) into the paged cache at positions prefix + t and computes
-    the same attention as ``extend_attention``, in one attention launch. Returns ``out``."""
+    the same attention as ``extend_attention``, in one attention launch. Returns ``out``.
+
+    ``check`` (default on) waits for the stream and raises if the launch's wait for
+    its appends gave up (``RuntimeError``) or a block id was outside
+    ``[0, num_blocks)`` (``ValueError``). A caller that turns it off to keep the
+    host ahead of the GPU passes its own ``workspace`` and calls ``read_status``
+    on it later."""
     lib, p, e, hkv, d, ws, args = _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale,
                                                out, lse, workspace, stream)
     total = int(e.sum())
@@ -385,4 +446,6 @@ def extend_attention_append(q, k_new, v_new, k_cache, v_cache, block_table, pref
         if tuple(t.shape) != (total, hkv, d) or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"{name} must be a contiguous device [sum(E), Hkv, D] tensor of q's dtype")
     _check(lib.extattn_extend_attention_append(args[0], k_new.data_ptr(), v_new.data_ptr(), *args[1:]))
+    if check:
+        _raise_on_status(ws, stream, "extend_attention_append")
     return out

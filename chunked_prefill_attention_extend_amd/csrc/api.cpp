@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <deque>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -36,24 +37,28 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 // Pinned host staging for the metadata copied into the caller's workspace.
-// A small ring of buffers per device; a buffer is reused only after the copy
-// that last read it has completed (tracked with an event).
+// Each device has a pool of pinned buffers; a buffer is reused only after the
+// copy that last read it has completed (an event per buffer). A call takes a
+// free buffer, or adds one to the pool, so it does not wait for the GPU; only
+// when kMaxStaging buffers are in flight on the device does it wait (on the
+// host, outside the pool's lock) for the oldest of them.
 struct StagingSlot {
   void* host = nullptr;
   size_t cap = 0;
   hipEvent_t done = nullptr;
-  bool pending = false;
 };
 
-constexpr int kRing = 8;
+constexpr int kMaxStaging = 512;
+constexpr size_t kStagingMinBytes = size_t(32) << 10;
 constexpr int kMaxDevices = 64;
 
 struct DeviceStaging {
-  StagingSlot slots[kRing];
-  int next = 0;
+  std::mutex mu;
+  std::vector<StagingSlot*> free_slots;
+  std::deque<StagingSlot*> in_flight;  // oldest first
+  int total = 0;
 };
 
-std::mutex g_staging_mu;
 DeviceStaging g_staging[kMaxDevices];
 
 int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
@@ -61,35 +66,72 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev < 0 || dev >= kMaxDevices) return fail(EXTATTN_EHIP, "device index out of range");
-  std::lock_guard<std::mutex> lock(g_staging_mu);
   DeviceStaging& ds = g_staging[dev];
-  StagingSlot& s = ds.slots[ds.next];
-  ds.next = (ds.next + 1) % kRing;
-  if (s.pending) {
-    e = hipEventSynchronize(s.done);
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (staging)");
-    s.pending = false;
+  StagingSlot* s = nullptr;
+  bool must_wait = false;
+  {
+    std::lock_guard<std::mutex> lock(ds.mu);
+    // buffers whose copies have completed go back to the free list
+    for (auto it = ds.in_flight.begin(); it != ds.in_flight.end();) {
+      if (hipEventQuery((*it)->done) == hipSuccess) {
+        ds.free_slots.push_back(*it);
+        it = ds.in_flight.erase(it);
+      } else {
+        ++it;
+      }
+    }
+    if (!ds.free_slots.empty()) {
+      s = ds.free_slots.back();
+      ds.free_slots.pop_back();
+    } else if (ds.total < kMaxStaging) {
+      s = new StagingSlot();
+      ++ds.total;
+    } else {
+      s = ds.in_flight.front();
+      ds.in_flight.pop_front();
+      must_wait = true;
+    }
   }
-  if (!s.done) {
-    e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreate (staging)");
+  // from here on the buffer belongs to this call alone; on failure it goes back
+  auto give_back = [&](int rc) {
+    std::lock_guard<std::mutex> lock(ds.mu);
+    ds.free_slots.push_back(s);
+    return rc;
+  };
+  if (must_wait) {
+    e = hipEventSynchronize(s->done);
+    if (e != hipSuccess) return give_back(hip_fail(e, "hipEventSynchronize (staging)"));
   }
-  if (s.cap < bytes) {
-    if (s.host) (void)hipHostFree(s.host);
-    s.host = nullptr;
-    s.cap = 0;
-    size_t cap = 1 << 16;
+  if (!s->done) {
+    e = hipEventCreateWithFlags(&s->done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      s->done = nullptr;
+      return give_back(hip_fail(e, "hipEventCreate (staging)"));
+    }
+  }
+  if (s->cap < bytes) {
+    if (s->host) (void)hipHostFree(s->host);
+    s->host = nullptr;
+    s->cap = 0;
+    size_t cap = kStagingMinBytes;
     while (cap < bytes) cap *= 2;
-    e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
-    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc (staging)");
-    s.cap = cap;
+    e = hipHostMalloc(&s->host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      s->host = nullptr;
+      return give_back(hip_fail(e, "hipHostMalloc (staging)"));
+    }
+    s->cap = cap;
   }
-  std::memcpy(s.host, src, bytes);
-  e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (metadata)");
-  e = hipEventRecord(s.done, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord (staging)");
-  s.pending = true;
+  std::memcpy(s->host, src, bytes);
+  e = hipMemcpyAsync(dst, s->host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return give_back(hip_fail(e, "hipMemcpyAsync (metadata)"));
+  e = hipEventRecord(s->done, stream);
+  if (e != hipSuccess) {
+    // the copy may still read the buffer: keep it out of the pool
+    return hip_fail(e, "hipEventRecord (staging)");
+  }
+  std::lock_guard<std::mutex> lock(ds.mu);
+  ds.in_flight.push_back(s);
   return EXTATTN_OK;
 }
 
@@ -132,6 +174,23 @@ int check_blocks(int32_t num_seqs, const int32_t* prefix, const int32_t* extend,
 extern "C" {
 
 const char* extattn_last_error(void) { return g_error.c_str(); }
+
+int extattn_read_status(const void* workspace, uint32_t* flags, int32_t* bad_block_reads, int32_t* exact_waves,
+                        void* stream) {
+  if (!workspace || !flags || !bad_block_reads || !exact_waves) return fail(EXTATTN_EINVAL, "null pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(EXTATTN_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int32_t words[3] = {0, 0, 0};
+  hipError_t e = hipMemcpyAsync(words, workspace, sizeof(words), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (status)");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (status)");
+  *flags = uint32_t(words[0]);
+  *bad_block_reads = words[1];
+  *exact_waves = words[2];
+  g_error.clear();
+  return EXTATTN_OK;
+}
 
 int extattn_token_budget_step(int32_t n_running, const int64_t* running_total, const int64_t* running_computed,
                               int32_t n_waiting, const int64_t* waiting_total, const int64_t* waiting_cached,
@@ -379,7 +438,9 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
     if (e != hipSuccess) return hip_fail(e, "fp32 attention launch");
   } else {
     if (a.n_items > 0) {
-      e = launch_attn_bf16(a, st);
+      // launches of chunk rows only (and their fused appends) run on the 4-wave chunk
+      // kernel; decode / verify rows need the mixed kernel, which takes every item
+      e = plan.n_split > 0 ? launch_attn_bf16(a, st) : launch_chunk_bf16(a, st);
       if (e != hipSuccess) return hip_fail(e, "bf16 attention launch");
     }
     if (a.n_tasks > 0) {

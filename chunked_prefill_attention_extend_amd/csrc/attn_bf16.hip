@@ -32,176 +32,9 @@
 // operand one 16-byte read of the slot-minor V cache layout.
 #include <type_traits>
 
-#include "device_common.hpp"
+#include "attn_bf16_common.hpp"
 
 namespace extattn {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr float kLn2 = 0.6931471805599453f;
-
-__device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                 c, 0, 0, 0);
-}
-
-__device__ inline uint32_t pack2(float lo, float hi) {
-  const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// Key (within a 32-key block) that MFMA row m of the S^T product holds.
-__device__ inline int key_of_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-// Key (within a 32-key block) of accumulator element i in lane half `hi`.
-__device__ inline int key_of_elem(int i, int hi) { return ((i >> 3) << 4) + (hi << 3) + (i & 7); }
-
-__device__ inline u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
-
-// Zero the bf16 values of a 16-byte V piece whose keys k0 .. k0+7 reach kv_len
-// (branch-free: a per-lane branch here would split the wave's control flow).
-__device__ inline u32x4 clip_keys(u32x4 v, int k0, int kv_len) {
-  const int n = kv_len - k0;  // keys of the piece that are inside
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t lo = (2 * w < n) ? 0x0000ffffu : 0u;
-    const uint32_t hi = (2 * w + 1 < n) ? 0xffff0000u : 0u;
-    v[w] &= (lo | hi);
-  }
-  return v;
-}
-
-// One online-softmax step over NKB 32-key blocks of raw scores.
-// m is kept in log2 units of the scaled scores; l is this lane's share of the
-// row sum (the two lanes of a row add theirs at the end).
-template <int NKB, int DB>
-__device__ inline void softmax_step(f32x16 (&s)[NKB], f32x16 (&o)[DB], float& m, float& l, float scale_log2,
-                                    u32x4 (&pf)[NKB][2]) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mnew = fmaxf(m, mx * scale_log2);
-  if (mnew > m) {
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 when m is -inf
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    l *= alpha;
-    m = mnew;
-  }
-  const float msafe = (m == -INFINITY) ? 0.f : m;
-  float ls = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int v = 0; v < 2; ++v)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * v + 2 * w], scale_log2, -msafe));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * v + 2 * w + 1], scale_log2, -msafe));
-        ls += p0 + p1;
-        pf[kb][v][w] = pack2(p0, p1);
-      }
-  l += ls;
-}
-
-// Write a finished row: either the final output (bf16) and lse, or a partial
-// slot (fp32 o normalised, natural-log lse) for the combine kernel.
-template <int D>
-__device__ inline void write_row(const AttnArgs& a, const f32x16 (&o)[D / 32], float m, float l, bool valid,
-                                 int hi, int64_t orow, int32_t slot, int32_t slot_rows, int rloc) {
-  constexpr int DB = D / 32;
-  const float lt = l + __shfl_xor(l, 32);
-  if (!valid) return;
-  if (slot < 0) {
-    const float inv = 1.f / lt;
-    uint16_t* op = static_cast<uint16_t*>(a.out) + orow * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int d = db * 32 + u * 8 + hi * 4;
-        u32x2 pk = {pack2(o[db][4 * u] * inv, o[db][4 * u + 1] * inv),
-                    pack2(o[db][4 * u + 2] * inv, o[db][4 * u + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + d) = pk;
-      }
-    if (hi == 0 && a.lse) a.lse[orow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
-  } else {
-    float* sl = a.slots + slot;  // rows [slot_rows][D], then lse [slot_rows]
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int d = db * 32 + u * 8 + hi * 4;
-        float4 v = {o[db][4 * u] * inv, o[db][4 * u + 1] * inv, o[db][4 * u + 2] * inv, o[db][4 * u + 3] * inv};
-        *reinterpret_cast<float4*>(sl + rloc * D + d) = v;
-      }
-    if (hi == 0) sl[slot_rows * D + rloc] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Chunk items: 256 rows, LDS-shared K/V tiles of 32 keys.
-//
-// K/V tiles go from the paged cache straight into LDS (global_load_lds_dwordx4:
-// each lane's 16 bytes land at the instruction's LDS base + 16 * lane), so no
-// registers hold the next tile. Each wave copies one 1 KB piece of every K and
-// every V tile. LDS layouts (per ring slot):
-//   K: 32 rows (keys) x D bf16; 16-byte piece p of row r sits at position
-//      p ^ swz_k(r), swz_k(r) = key_of_row(r % 16) (mod pieces per row).
-//   V: two sub-tiles, one per 16-key block, each D rows (features) x 16 keys;
-//      half h (8 keys) of row d sits at position h ^ swz_v(d),
-//      swz_v(d) = ((d >> 2) ^ (d >> 3)) & 1.
-// A piece lies inside one cache block, so every direct load has a uniform base
-// address and a 32-bit per-lane offset. Both swizzles keep every aligned group
-// of 8 (and of 16) lanes of a 16-byte LDS read on distinct banks. Invalid block
-// ids and tiles past the range read a page of zeros; keys past the range are
-// masked in the scores, and values past the sequence end are cleared in LDS.
-// ---------------------------------------------------------------------------
-__device__ inline int swz_v(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
-
-// Value of lane l ^ 32 (the other lane holding the same query row).
-// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes 0..31
-// of its second; either result then holds the partner value in the lane half that
-// received it, whether or not both operands share a register.
-__device__ inline float partner(float x, int hi) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
-                                                  false, false);
-  const uint32_t v = hi ? r[0] : r[1];
-  return __builtin_bit_cast(float, v);
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// LDS byte address of a pointer into the workgroup's shared memory, as a wave-uniform value.
-__device__ inline uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p)));
-}
-
-// Direct copies from global memory into LDS: lane l's 16 (or 4) bytes at base + off
-// land at LDS address lds + 16 l (4 l). They are issued as inline assembly on purpose:
-// the compiler's wait-count pass treats any direct-to-LDS load it sees as a possible
-// producer of every later LDS read and then drains all LDS reads before each use
-// (s_waitcnt lgkmcnt(0)), which serialises the MFMA operand reads. The kernel orders
-// these copies itself (s_waitcnt vmcnt and a barrier before the data is read); loads
-// the compiler does not know about only make its own vmcnt waits stricter.
-__device__ inline void dma16(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
-}
-__device__ inline void dma4(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
-}
-
-// Bound on one lane's row sum of a chunk tile's 16 weights. Below it every weight is
-// at most 2^12, so O and l stay far from fp32 overflow; above it (or when a weight
-// overflowed to inf) the running max is raised before the weights are used.
-constexpr float kSumBound = 4096.0f;
 
 template <int D>
 __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char* smem) {
@@ -239,21 +72,13 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   const int lim_min = min(si.prefix + it.row0 / G, it.key_end - 1);
   const float c2 = a.scale_log2;
 
+  // Query rows enter the products exactly as given (bf16); the softmax scale is
+  // applied to the fp32 scores, inside the exponent.
   u32x4 qf[KS];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + orow * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = valid ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : zero4();
-    // The softmax scale in log2 units goes into Q once (rounded to bf16, nearest even),
-    // so scores leave the product scaled. The rounding moves a score by about 2^-9 of
-    // its terms' spread, well below the effect of the weights' own bf16 rounding.
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t u = qf[ks][e];
-        qf[ks][e] = pack2(__uint_as_float(u << 16) * c2, __uint_as_float(u & 0xffff0000u) * c2);
-      }
   }
 
   const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
@@ -297,7 +122,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     const bool inside = (t0 + 32 * k) * (KT / kBlockSize) + lane < nblk;
     const bool ok = block_ok(v, a.num_blocks);
     const uint64_t bad = __builtin_amdgcn_ballot_w64(inside && !ok);
-    if (bad != 0 && wave == 0 && lane == 0) atomicAdd(a.err, int(__builtin_popcountll(bad)));
+    if (bad != 0 && wave == 0 && lane == 0) report_bad_blocks(a.err, int(__builtin_popcountll(bad)));
     // tiles past the range (padding steps) read the zero page even where the
     // sequence still has keys
     const bool in_range = t0 + 32 * k + (lane >> 1) < t1;
@@ -346,9 +171,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   // sum l. m is the exact row max of the first tile; afterwards it is raised only
   // when a tile's weights grow past kSumBound (rare), so no tile needs a row max.
   float m = 0.f, l = 0.f;
-  // -m in every accumulator element: the QK product of a tile starts from it, so
-  // its scores come out shifted
-  f32x16 negm = f32x16{};
+  float mneg = 0.f;  // -m: the weights are 2^(s c - m), one fma and one exp2 per score
 
   // S^T of one tile from K ring slot `slot` (compile-time). Invalid blocks were
   // loaded from the zero page; keys past the sequence end are masked later.
@@ -382,19 +205,19 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
         if (key_of_elem(i, 0) > t) s[i] = -INFINITY;
     }
   };
-  // Scores leave their QK product shifted, s c - m (log2 units): Q carries the scale
-  // and the product starts from -m. Weights p = 2^s as packed bf16 for the P.V
-  // product, and this lane's fp32 sum of them over the tile, taken before the
-  // rounding (lse carries no rounding of the weights; the normaliser is within 2^-9
-  // relative of the rounded weights' sum).
+  // Scores leave their QK product as raw fp32 dot products s. Weights
+  // p = 2^(s c - m), c = scale * log2(e), as packed bf16 for the P.V product, and this
+  // lane's fp32 sum of them over the tile, taken before the rounding (lse carries no
+  // rounding of the weights; the normaliser is within 2^-9 relative of the rounded
+  // weights' sum).
   auto weights = [&](const f32x16& s, u32x4 (&pf)[2], float& ls) {
     float l0 = 0.f, l1 = 0.f;
 #pragma unroll
     for (int v = 0; v < 2; ++v)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float p0 = __builtin_amdgcn_exp2f(s[8 * v + 2 * w]);
-        const float p1 = __builtin_amdgcn_exp2f(s[8 * v + 2 * w + 1]);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * v + 2 * w], c2, mneg));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * v + 2 * w + 1], c2, mneg));
         pf[v][w] = pack2(p0, p1);
         l0 += p0;
         l1 += p1;
@@ -402,23 +225,20 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     ls = l0 + l1;
   };
   // Check of a tile's weights before they enter P.V: when some lane's sum passed
-  // kSumBound (or overflowed), raise m by the rows' exact max over the (shifted)
-  // tile, rescale O and l, shift the tile again and redo its weights (the next
-  // tile's products start from the new m). Then add the sum to l.
-  auto check = [&](f32x16& s, u32x4 (&pf)[2], float& ls) {
+  // kSumBound (or overflowed), raise m to the rows' exact max over the tile, rescale
+  // O and l and redo the tile's weights (the next tile's weights use the new m).
+  // Then add the sum to l.
+  auto check = [&](const f32x16& s, u32x4 (&pf)[2], float& ls) {
     if (__builtin_amdgcn_ballot_w64(ls > kSumBound) != 0) {
       float mx = row_max(s);
       mx = fmaxf(mx, partner(mx, hi));
-      const float d = fmaxf(mx, 0.f);
+      const float d = fmaxf(fmaf(mx, c2, mneg), 0.f);  // masked rows: -inf -> 0
       const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       l *= alpha;
       m += d;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] -= d;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) negm[i] = -m;
+      mneg = -m;
       weights(s, pf, ls);
     }
     l += ls;
@@ -487,17 +307,13 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
       mask(t0, sa);
       float mx = row_max(sa);
       mx = fmaxf(mx, partner(mx, hi));
-      m = (mx == -INFINITY) ? 0.f : mx;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sa[i] -= m;
-        negm[i] = -m;
-      }
+      m = (mx == -INFINITY) ? 0.f : mx * c2;
+      mneg = -m;
       weights(sa, pa, la);
     }
     // Steady step u (tile j = t0 + u, not the last): S(j) is in scur (masked) and its
     // weights in pcur / lcur, K(j+1) in K slot (u+1)%4, V(j) in V slot u%4. Then
-    //   check tile j's weights (rare path: raise m before the next products),
+    //   check tile j's weights (rare path: raise m before the next weights),
     //   region A: S(j+1) = QK(j+1) MFMAs, with the copies of K(j+3) and V(j+2) (their
     //     slots were last read two steps ago) issued half way,
     //   mask tile j+1 if diagonal,
@@ -538,7 +354,7 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             if (ks + 3 < KS) kf[ks + 3] = *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ ((ks + 3) << 5)));
-            snext = mfma32(kf[ks], qf[ks], ks == 0 ? negm : snext);
+            snext = mfma32(kf[ks], qf[ks], ks == 0 ? f32x16{} : snext);
             if (ks == KS / 2 - 1) issue();
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -581,8 +397,8 @@ __device__ void chunk_item(const AttnArgs& a, const WorkItem& it, unsigned char*
 #pragma unroll
             for (int pp = lo(i); pp < lo(i + 1); ++pp) {
               const int v = pp >> 2, w = pp & 3;
-              e[2 * pp] = __builtin_amdgcn_exp2f(snext[8 * v + 2 * w]);
-              e[2 * pp + 1] = __builtin_amdgcn_exp2f(snext[8 * v + 2 * w + 1]);
+              e[2 * pp] = __builtin_amdgcn_exp2f(fmaf(snext[8 * v + 2 * w], c2, mneg));
+              e[2 * pp + 1] = __builtin_amdgcn_exp2f(fmaf(snext[8 * v + 2 * w + 1], c2, mneg));
             }
             if (i > 0) {
 #pragma unroll
@@ -700,7 +516,7 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     const int32_t v = inside ? bt[lb] : -1;
     const bool ok = block_ok(v, a.num_blocks);
     const uint64_t bad = __builtin_amdgcn_ballot_w64(inside && !ok);
-    if (bad != 0 && lane == 0) atomicAdd(a.err, int(__builtin_popcountll(bad)));
+    if (bad != 0 && lane == 0) report_bad_blocks(a.err, int(__builtin_popcountll(bad)));
     idw = (inside && ok) ? v : -1;
   }
   const unsigned char* zp = static_cast<const unsigned char*>(a.zero_page);
@@ -875,73 +691,6 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   }
 }
 
-// ---------------------------------------------------------------------------
-// Fused append. Append items copy new tokens of one request from k_new / v_new
-// into the paged cache (K as one 16-byte store per piece, V scattered into the
-// slot-minor layout), then each wave adds 1 to the completion counter with
-// release semantics at device scope. An attention item whose key range reaches
-// the request's new keys waits, before its first load, until the counter says
-// that every append wave is done. The append items lead the launch order and
-// every die dispatches its workgroups in order, so the waits end; the wait is
-// still bounded and leaves kErrWaitTimeout in the error word if it gives up.
-// ---------------------------------------------------------------------------
-template <int D>
-__device__ void append_item(const AttnArgs& a, const WorkItem& it) {
-  constexpr int PIECES = D / 8;  // 16-byte pieces of a head vector
-  const SeqInfo si = a.seqs[it.seq];
-  const int per_tok = a.hkv * PIECES;
-  const int n = it.nrows * per_tok;
-  const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const int t = i / per_tok;
-    const int rem = i - t * per_tok;
-    const int g = rem / PIECES, c = rem - g * PIECES;
-    const int tok = it.row0 + t;  // new token index within the request
-    const int pos = si.prefix + tok;
-    const int32_t phys = bt[pos / kBlockSize];
-    if (!block_ok(phys, a.num_blocks)) {
-      if (g == 0 && c == 0) atomicAdd(a.err, 1);
-      continue;
-    }
-    const int slot = pos % kBlockSize;
-    const int64_t src = (int64_t(si.q_off + tok) * a.hkv + g) * D + c * 8;
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k_new) + src);
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v_new) + src);
-    uint16_t* kc = static_cast<uint16_t*>(a.k_cache_w) + ((int64_t(phys) * a.hkv + g) * kBlockSize + slot) * D + c * 8;
-    *reinterpret_cast<u32x4*>(kc) = kv;
-    uint16_t* vc = static_cast<uint16_t*>(a.v_cache_w) + (int64_t(phys) * a.hkv + g) * int64_t(D) * kBlockSize +
-                   int64_t(c * 8) * kBlockSize + slot;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t w = vv[e];
-      vc[(2 * e) * kBlockSize] = uint16_t(w & 0xFFFFu);
-      vc[(2 * e + 1) * kBlockSize] = uint16_t(w >> 16);
-    }
-  }
-  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(a.append_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-constexpr int kWaitSpinLimit = 1 << 20;  // polls, ~0.3 us apart: ~0.3 s
-
-// One lane polls the counter (relaxed, spaced out so that hundreds of waiting
-// workgroups do not flood one address), then one acquire fence makes the appended
-// K/V visible before the workgroup's first load.
-__device__ void wait_appends(const AttnArgs& a) {
-  if (threadIdx.x == 0) {
-    const int target = a.n_append * kWaves;
-    int spins = 0;
-    while (__hip_atomic_load(a.append_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(10);
-      if (++spins == kWaitSpinLimit) {
-        atomicOr(a.err, kErrWaitTimeout);
-        break;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-}
-
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
@@ -958,9 +707,9 @@ void attn_bf16_kernel(AttnArgs a) {
     st[3] = it.seq;
   }
   if (it.kind == kItemAppend) {
-    append_item<D>(a, it);
+    append_item<D, kWaves>(a, it);
   } else {
-    if (a.n_append > 0 && it.key_end > a.seqs[it.seq].prefix) wait_appends(a);  // reads new keys
+    if (a.n_append > 0 && it.key_end > a.seqs[it.seq].prefix) wait_appends<kWaves>(a);  // reads new keys
     if (it.kind == kItemChunk)
       chunk_item<D>(a, it, smem);
     else if (it.nrows <= kSplitRows)

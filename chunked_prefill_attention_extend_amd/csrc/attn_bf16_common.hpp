@@ -1,0 +1,209 @@
+// Device helpers of the bf16 attention kernels: MFMA wrappers, the key order
+// inside a 32-key tile, LDS swizzles and direct-to-LDS copies, the row epilogue,
+// and the fused append's copy and wait.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace extattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+__device__ inline uint32_t pack2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Key (within a 32-key block) that MFMA row m of the S^T product holds.
+__device__ inline int key_of_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Key (within a 32-key block) of accumulator element i in lane half `hi`.
+__device__ inline int key_of_elem(int i, int hi) { return ((i >> 3) << 4) + (hi << 3) + (i & 7); }
+
+__device__ inline u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// Zero the bf16 values of a 16-byte V piece whose keys k0 .. k0+7 reach kv_len
+// (branch-free: a per-lane branch here would split the wave's control flow).
+__device__ inline u32x4 clip_keys(u32x4 v, int k0, int kv_len) {
+  const int n = kv_len - k0;  // keys of the piece that are inside
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = (2 * w < n) ? 0x0000ffffu : 0u;
+    const uint32_t hi = (2 * w + 1 < n) ? 0xffff0000u : 0u;
+    v[w] &= (lo | hi);
+  }
+  return v;
+}
+
+// Write a finished row: either the final output (bf16) and lse, or a partial
+// slot (fp32 o normalised, natural-log lse) for the combine kernel.
+template <int D>
+__device__ inline void write_row(const AttnArgs& a, const f32x16 (&o)[D / 32], float m, float l, bool valid,
+                                 int hi, int64_t orow, int32_t slot, int32_t slot_rows, int rloc) {
+  constexpr int DB = D / 32;
+  const float lt = l + __shfl_xor(l, 32);
+  if (!valid) return;
+  if (slot < 0) {
+    const float inv = 1.f / lt;
+    uint16_t* op = static_cast<uint16_t*>(a.out) + orow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int d = db * 32 + u * 8 + hi * 4;
+        u32x2 pk = {pack2(o[db][4 * u] * inv, o[db][4 * u + 1] * inv),
+                    pack2(o[db][4 * u + 2] * inv, o[db][4 * u + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + d) = pk;
+      }
+    if (hi == 0 && a.lse) a.lse[orow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+  } else {
+    float* sl = a.slots + slot;  // rows [slot_rows][D], then lse [slot_rows]
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int d = db * 32 + u * 8 + hi * 4;
+        float4 v = {o[db][4 * u] * inv, o[db][4 * u + 1] * inv, o[db][4 * u + 2] * inv, o[db][4 * u + 3] * inv};
+        *reinterpret_cast<float4*>(sl + rloc * D + d) = v;
+      }
+    if (hi == 0) sl[slot_rows * D + rloc] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk items: 256 rows, LDS-shared K/V tiles of 32 keys.
+//
+// K/V tiles go from the paged cache straight into LDS (global_load_lds_dwordx4:
+// each lane's 16 bytes land at the instruction's LDS base + 16 * lane), so no
+// registers hold the next tile. Each wave copies one 1 KB piece of every K and
+// every V tile. LDS layouts (per ring slot):
+//   K: 32 rows (keys) x D bf16; 16-byte piece p of row r sits at position
+//      p ^ swz_k(r), swz_k(r) = key_of_row(r % 16) (mod pieces per row).
+//   V: two sub-tiles, one per 16-key block, each D rows (features) x 16 keys;
+//      half h (8 keys) of row d sits at position h ^ swz_v(d),
+//      swz_v(d) = ((d >> 2) ^ (d >> 3)) & 1.
+// A piece lies inside one cache block, so every direct load has a uniform base
+// address and a 32-bit per-lane offset. Both swizzles keep every aligned group
+// of 8 (and of 16) lanes of a 16-byte LDS read on distinct banks. Invalid block
+// ids and tiles past the range read a page of zeros; keys past the range are
+// masked in the scores, and values past the sequence end are cleared in LDS.
+// ---------------------------------------------------------------------------
+__device__ inline int swz_v(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
+
+// Value of lane l ^ 32 (the other lane holding the same query row).
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes 0..31
+// of its second; either result then holds the partner value in the lane half that
+// received it, whether or not both operands share a register.
+__device__ inline float partner(float x, int hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  const uint32_t v = hi ? r[0] : r[1];
+  return __builtin_bit_cast(float, v);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS byte address of a pointer into the workgroup's shared memory, as a wave-uniform value.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p)));
+}
+
+// Direct copies from global memory into LDS: lane l's 16 (or 4) bytes at base + off
+// land at LDS address lds + 16 l (4 l). They are issued as inline assembly on purpose:
+// the compiler's wait-count pass treats any direct-to-LDS load it sees as a possible
+// producer of every later LDS read and then drains all LDS reads before each use
+// (s_waitcnt lgkmcnt(0)), which serialises the MFMA operand reads. The kernel orders
+// these copies itself (s_waitcnt vmcnt and a barrier before the data is read); loads
+// the compiler does not know about only make its own vmcnt waits stricter.
+__device__ inline void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
+}
+__device__ inline void dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
+}
+
+// Bound on one lane's row sum of a chunk tile's 16 weights. Below it every weight is
+// at most 2^12, so O and l stay far from fp32 overflow; above it (or when a weight
+// overflowed to inf) the running max is raised before the weights are used.
+constexpr float kSumBound = 4096.0f;
+
+// ---------------------------------------------------------------------------
+// Fused append. Append items copy new tokens of one request from k_new / v_new
+// into the paged cache (K as one 16-byte store per piece, V scattered into the
+// slot-minor layout), then each wave adds 1 to the completion counter with
+// release semantics at device scope. An attention item whose key range reaches
+// the request's new keys waits, before its first load, until the counter says
+// that every append wave is done. The append items lead the launch order and
+// every die dispatches its workgroups in order, so the waits end; the wait is
+// still bounded and sets kStatusWaitTimeout in the status flags if it gives up.
+// ---------------------------------------------------------------------------
+template <int D, int WAVES>
+__device__ void append_item(const AttnArgs& a, const WorkItem& it) {
+  constexpr int PIECES = D / 8;  // 16-byte pieces of a head vector
+  const SeqInfo si = a.seqs[it.seq];
+  const int per_tok = a.hkv * PIECES;
+  const int n = it.nrows * per_tok;
+  const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
+  for (int i = threadIdx.x; i < n; i += 64 * WAVES) {
+    const int t = i / per_tok;
+    const int rem = i - t * per_tok;
+    const int g = rem / PIECES, c = rem - g * PIECES;
+    const int tok = it.row0 + t;  // new token index within the request
+    const int pos = si.prefix + tok;
+    const int32_t phys = bt[pos / kBlockSize];
+    if (!block_ok(phys, a.num_blocks)) {
+      if (g == 0 && c == 0) report_bad_blocks(a.err, 1);
+      continue;
+    }
+    const int slot = pos % kBlockSize;
+    const int64_t src = (int64_t(si.q_off + tok) * a.hkv + g) * D + c * 8;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k_new) + src);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v_new) + src);
+    uint16_t* kc = static_cast<uint16_t*>(a.k_cache_w) + ((int64_t(phys) * a.hkv + g) * kBlockSize + slot) * D + c * 8;
+    *reinterpret_cast<u32x4*>(kc) = kv;
+    uint16_t* vc = static_cast<uint16_t*>(a.v_cache_w) + (int64_t(phys) * a.hkv + g) * int64_t(D) * kBlockSize +
+                   int64_t(c * 8) * kBlockSize + slot;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = vv[e];
+      vc[(2 * e) * kBlockSize] = uint16_t(w & 0xFFFFu);
+      vc[(2 * e + 1) * kBlockSize] = uint16_t(w >> 16);
+    }
+  }
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(a.append_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kWaitSpinLimit = 1 << 20;  // polls, ~0.3 us apart: ~0.3 s
+
+// One lane polls the counter (relaxed, spaced out so that hundreds of waiting
+// workgroups do not flood one address), then one acquire fence makes the appended
+// K/V visible before the workgroup's first load.
+template <int WAVES>
+__device__ void wait_appends(const AttnArgs& a) {
+  if (threadIdx.x == 0) {
+    const int target = a.n_append * WAVES;
+    int spins = 0;
+    while (__hip_atomic_load(a.append_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(10);
+      if (++spins == kWaitSpinLimit) {
+        atomicOr(a.err, kStatusWaitTimeout);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+}  // namespace extattn

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
         sc = acc * a.scale;
       } else {
         sc = 0.f;
-        if (key % kBlockSize == 0 && h == 0) atomicAdd(a.err, 1);
+        if (key % kBlockSize == 0 && h == 0) report_bad_blocks(a.err, 1);
       }
     }
     const float mnew = fmaxf(m, wave_max(sc));  // lane 0's key kb <= lim, so finite

@@ -25,4 +25,10 @@ __device__ inline bool block_ok(int32_t phys, int64_t num_blocks) {
   return phys >= 0 && int64_t(phys) < num_blocks;
 }
 
+// Report n invalid block-id reads in the status words (flag, then count).
+__device__ inline void report_bad_blocks(int32_t* status, int n) {
+  atomicOr(status, kStatusBadBlock);
+  atomicAdd(status + 1, n);
+}
+
 }  // namespace extattn

@@ -44,7 +44,11 @@ enum : int32_t {
 
 constexpr int kAppendTokens = 16;  // tokens per append item of a fused append + attention launch
 constexpr int kAppendDoneOffset = 128;  // byte offset of the append completion counter in the workspace header
-constexpr int32_t kErrWaitTimeout = 1 << 30;  // error-word bit: an attention item stopped waiting for the appends
+// Status words at the start of the workspace (reset by every call's metadata upload):
+// word 0 holds flags, word 1 counts invalid block-id reads (wrapping), word 2 counts
+// the waves that redid their rows on the exact two-pass path (informational).
+constexpr int32_t kStatusBadBlock = 1;     // a block id outside [0, num_blocks) was met
+constexpr int32_t kStatusWaitTimeout = 2;  // an attention item stopped waiting for the fused appends
 
 // One workgroup's work. Rows are flattened per (request, KV head) as
 // row = pos * group + head_in_group, pos in [0, E), head_in_group in [0, group).
@@ -142,6 +146,7 @@ struct Plan {
   int64_t n_slot_floats = 0;  // size of the partial-slot area
   int32_t split_keys = 0;  // keys per split workgroup (0: no split items)
   int32_t n_append = 0;    // append items at the head of `items` (fused append launch)
+  int32_t n_split = 0;     // split items (decode / verify rows) in `items`
   int64_t total_rows = 0;
   // byte offsets inside the workspace
   size_t off_zero = 0, off_seqs = 0, off_items = 0, off_tasks = 0, off_slots = 0, bytes = 0, upload_bytes = 0;
@@ -188,6 +193,7 @@ int decode_first_with_slack_impl(int64_t ready_decode, int64_t pending_prefill, 
 
 // kernel launchers (one per .hip file)
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16(const AttnArgs& a, hipStream_t stream);  // chunk and append items only
 hipError_t launch_combine(const AttnArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const KvArgs& a, int32_t dtype, hipStream_t stream);

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvArgs a) {
         phys = p;
         slot = pos % kBlockSize;
       } else {
-        atomicAdd(a.err, 1);  // one count per token whose block id is invalid
+        report_bad_blocks(a.err, 1);  // one count per token whose block id is invalid
       }
     }
     s_phys[tid] = phys;

@@ -80,6 +80,8 @@ int make_launch_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* ext
                      int32_t head_dim, int32_t dtype, LaunchPlan& lp) {
   const int rc = build_plan(num_seqs, prefix, extend, hq, hkv, head_dim, dtype, lp.plan, true);
   if (rc != EXTATTN_OK) return rc;
+  lp.plan.n_split = 0;
+  for (const WorkItem& it : lp.plan.items) lp.plan.n_split += it.kind == kItemSplit ? 1 : 0;
   const Plan& p = lp.plan;
   lp.blob.assign(p.upload_bytes, 0);
   std::memcpy(lp.blob.data() + p.off_seqs, p.seqs.data(), sizeof(SeqInfo) * p.seqs.size());

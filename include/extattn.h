@@ -24,10 +24,18 @@
  *    owns every buffer. Device work is enqueued on `stream` (a hipStream_t;
  *    NULL means the default stream) and the call returns without waiting;
  *    outputs are valid once the stream has reached that point. The library
- *    keeps pinned host staging buffers of its own for the small metadata it
- *    copies to the workspace (allocated on first use, reused afterwards), and
- *    a bounded host table of launch plans keyed by the launch's shape (see
- *    extattn_plan_cache_configure).
+ *    keeps a pool of pinned host staging buffers per device for the small
+ *    metadata it copies to the workspace (a buffer is reused once the copy
+ *    that last read it has completed; the pool grows instead of waiting, up to
+ *    512 buffers in flight per device, beyond which a call waits on the host
+ *    for the oldest copy to finish), and a bounded host table of launch plans
+ *    keyed by the launch's shape (see extattn_plan_cache_configure).
+ *  - Status words. Invalid input that only the GPU can see (a block id outside
+ *    [0, num_blocks) in a row the launch reads) and a fused-append wait that
+ *    gave up are not silent: each call that takes a workspace clears the first
+ *    12 bytes of it (before its kernels run, in stream order) and its kernels
+ *    record such events there; extattn_read_status returns them. Results of a
+ *    call whose flags are not zero are not valid.
  *  - Element types: EXTATTN_BF16 (bfloat16) or EXTATTN_F32 (float). q, the
  *    caches and out share one element type; lse is always float.
  *  - Heads: num_q_heads must be a multiple of num_kv_heads; query head h reads
@@ -62,6 +70,12 @@ enum {
 };
 
 enum { EXTATTN_BF16 = 0, EXTATTN_F32 = 1 };
+
+/* Status flags (see extattn_read_status). */
+enum {
+  EXTATTN_STATUS_BAD_BLOCK = 1,   /* a block id outside [0, num_blocks) was read */
+  EXTATTN_STATUS_WAIT_TIMEOUT = 2 /* a fused-append wait gave up; results are not valid */
+};
 
 /* Entry kinds of extattn_mixed_chunk_step. */
 enum { EXTATTN_ENTRY_DECODE = 0, EXTATTN_ENTRY_CHUNKED = 1, EXTATTN_ENTRY_WAITING = 2 };
@@ -213,8 +227,8 @@ size_t extattn_kv_append_workspace_bytes(int32_t num_seqs);
  *                request r goes to logical position prefix_lens[r] + t.
  * k_cache, v_cache, block_table, max_blocks, num_blocks: the paged cache (see
  *                the layout above). Physical ids outside [0, num_blocks) are
- *                skipped (nothing written) and counted in the workspace's
- *                error word.
+ *                skipped (nothing written) and reported in the workspace's
+ *                status words (EXTATTN_STATUS_BAD_BLOCK).
  * prefix_lens, extend_lens: host [num_seqs], prefix >= 0, extend >= 0.
  * workspace:     device, at least extattn_kv_append_workspace_bytes(num_seqs).
  * Errors: EXTATTN_EINVAL for null pointers, num_seqs < 1, negative lengths,
@@ -243,18 +257,20 @@ int extattn_kv_append(const void* k_new, const void* v_new, void* k_cache, void*
  *
  * q:            device [sum(E), Hq, D]
  * k_cache, v_cache, block_table, max_blocks, num_blocks: the paged cache.
- *               Block ids outside [0, num_blocks) read as zeros and are counted
- *               in the workspace's error word.
+ *               Block ids outside [0, num_blocks) read as zeros and are
+ *               reported in the workspace's status words
+ *               (EXTATTN_STATUS_BAD_BLOCK; the results are then not valid).
  * prefix_lens, extend_lens: host [num_seqs]; prefix >= 0, extend >= 1.
  * scale:        finite and > 0 (the pages use 1/sqrt(D)).
  * out:          device [sum(E), Hq, D], element type of q.
  * lse:          device [sum(E), Hq] float, or NULL to skip.
  * workspace:    device, at least the extattn_workspace_bytes() result, 256-byte
- *               aligned; its first 4 bytes hold the error word after the call.
- * Accumulation is fp32 for both element types. For bf16, the query rows of
- * chunk tiles are multiplied by scale * log2(e) and rounded to bf16 before the
- * Q.K product, and the softmax weights are rounded to bf16 before the P.V
- * product.
+ *               aligned; its first 8 bytes hold the status words after the call
+ *               (extattn_read_status).
+ * Accumulation is fp32 for both element types. The scores are the fp32 dot
+ * products of the given q and k; the scale is applied to them in fp32 inside the
+ * exponent. For bf16 the softmax weights are rounded to bf16 for the P.V product
+ * only; lse and the normaliser sum the fp32 weights.
  * Errors: EXTATTN_EINVAL for null required pointers, num_seqs < 1, any
  * extend < 1 or prefix < 0, Hq % Hkv != 0, a request needing more than
  * max_blocks blocks, a non-finite or non-positive scale, sum(E) above 2^31-1;
@@ -279,16 +295,16 @@ int extattn_extend_attention(const void* q, const void* k_cache, const void* v_c
  * first workgroups write them into the paged cache and the attention
  * workgroups that reach a request's new keys wait until those writes are done
  * (a device-scope counter in the workspace, release / acquire; the wait is
- * bounded: if it gives up, bit 30 of the error word is set and the results are
- * not valid). Prefix keys need no wait.
+ * bounded: if it gives up, EXTATTN_STATUS_WAIT_TIMEOUT is set in the status
+ * words and the results are not valid). Prefix keys need no wait.
  *
  * k_new, v_new: device [sum(E), Hkv, D], element type of q, request order;
  *               token q_off_r + t of request r goes to position prefix_lens[r] + t.
  * k_cache, v_cache: written (the new tokens' slots) and read.
  * Other arguments, ownership and errors as for extattn_extend_attention; the
  * workspace size is the same extattn_workspace_bytes() result. Block ids
- * outside [0, num_blocks) are skipped for writing and read as zeros, and
- * counted in the error word. fp32 runs the append as its own launch first on
+ * outside [0, num_blocks) are skipped for writing, read as zeros and reported
+ * (EXTATTN_STATUS_BAD_BLOCK). fp32 runs the append as its own launch first on
  * the same stream.
  */
 int extattn_extend_attention_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
@@ -327,6 +343,31 @@ int extattn_extend_attention_timed(const void* q, const void* k_cache, const voi
                                    void* out, float* lse, void* workspace, size_t workspace_bytes,
                                    void* stream, int64_t* stamps, int32_t capacity, int32_t* n_items,
                                    double* tick_hz);
+
+/*
+ * Status of the last call that used `workspace` (any call taking a workspace:
+ * extattn_kv_append, extattn_extend_attention and its _append / _timed
+ * variants). The msmodeling chunked-prefill RFC, section 2.4 (reliability:
+ * invalid input is reported at the entry with a clear error, never swallowed),
+ * asks for this for the checks that only the GPU can make.
+ *
+ * Enqueues a copy of the workspace's two status words on `stream`, then waits
+ * on the host until the stream has completed it (hipStreamSynchronize): call
+ * it where a host wait is acceptable (tests, a periodic health check, after a
+ * fused-append call whose results matter).
+ * flags:            host out, EXTATTN_STATUS_* bits (0: nothing to report).
+ * bad_block_reads:  host out, number of invalid block-id reads recorded (each
+ *                   workgroup that meets one counts it; wraps past 2^31 - 1).
+ * exact_waves:      host out, number of waves of chunk rows that redid their
+ *                   rows on the exact two-pass path because a tile's weights grew
+ *                   past 2^64 against the first tile's row max (scores rising by
+ *                   more than 64 in log2 units along the keys). Informational:
+ *                   the results are valid; the count shows where time went.
+ * Errors: EXTATTN_EINVAL for null pointers or a workspace not 256-byte
+ * aligned; EXTATTN_EHIP if the copy or the wait fails.
+ */
+int extattn_read_status(const void* workspace, uint32_t* flags, int32_t* bad_block_reads, int32_t* exact_waves,
+                        void* stream);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char* extattn_last_error(void);

@@ -20,12 +20,16 @@ from synth import Workload
 
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
-# Tolerances on the output: bf16 inputs with fp32 accumulation, and fp32.
-# lse (natural log) for bf16: the row sum adds the softmax weights after their
-# rounding to bf16 (relative error <= 2^-9 each, nearest even), so the sum is off by
-# a factor within 1 +- 2^-9 and lse by at most 2^-9 ~ 1.95e-3, plus fp32 terms ~1e-6.
+# Tolerances. out: the benchmark spec's bars for bf16 inputs with fp32 accumulation
+# (max abs 2e-2, mean abs 2e-3) and for fp32 (1e-5). lse (natural log): 1e-3 for
+# bf16 inputs, 1e-5 for fp32, against the exact fp64 log-sum-exp of the scaled
+# scores. The kernels form every score from the unmodified inputs and sum the
+# fp32 weights before rounding them for the P.V product, so lse carries only fp32
+# rounding (scale * log2 e to fp32, the exponent's fma, exp2 / log2, and the sum
+# over up to 2^17 keys), far inside 1e-3 for the pages' score ranges; the largest
+# |lse| seen by these tests is a few hundred, whose fp32 spacing is 3e-5.
 TOL = {
-    "bf16": {"max": 2e-2, "mean": 2e-3, "lse": 2e-3},
+    "bf16": {"max": 2e-2, "mean": 2e-3, "lse": 1e-3},
     "f32": {"max": 1e-5, "mean": 1e-5, "lse": 1e-5},
 }
 
@@ -46,6 +50,7 @@ class PagedCache:
 
     def __init__(self, w: Workload, device="cuda", fill=float("nan"), block_table: np.ndarray | None = None):
         self.w = w
+        self.expect_fast = True
         dt = TORCH_DT[w.dtype]
         self.k = torch.full((w.num_blocks, w.n_kv_heads, w.block_size, w.head_dim), fill, dtype=dt, device=device)
         self.v = torch.full((w.num_blocks, w.n_kv_heads, w.head_dim, w.block_size), fill, dtype=dt, device=device)
@@ -60,7 +65,7 @@ class PagedCache:
                extend: list[int]) -> None:
         bt = self.bt if list(req_idx) == list(range(self.bt_host.shape[0])) else self.rows(req_idx)
         ext.kv_append(dev_tensor(k_rows, self.w.dtype), dev_tensor(v_rows, self.w.dtype), self.k, self.v, bt,
-                      prefix, extend)
+                      prefix, extend, check=True)
 
     def attend(self, req_idx: list[int], prefix: list[int], extend: list[int], q_rows: np.ndarray):
         w = self.w
@@ -68,7 +73,11 @@ class PagedCache:
         q = dev_tensor(q_rows, w.dtype)
         out = torch.empty_like(q)
         lse = torch.empty((q.shape[0], w.n_q_heads), dtype=torch.float32, device=q.device)
-        ext.extend_attention(q, self.k, self.v, bt, prefix, extend, w.scale, out, lse)
+        ext.extend_attention(q, self.k, self.v, bt, prefix, extend, w.scale, out, lse, check=True)
+        # the pages' workloads keep every tile's weights far inside the fast loop's
+        # bound: no wave may take the exact two-pass path
+        if self.expect_fast:
+            assert ext.last_status()[2] == 0, f"{ext.last_status()[2]} waves took the exact path"
         return out, lse
 
 

@@ -4,7 +4,7 @@
 ``kv_append`` does and give the same ``out`` / ``lse`` bit for bit as
 ``kv_append`` followed by ``extend_attention`` (the attention work items are
 the same; only where the new tokens' K/V come from in time differs), with no
-error word set. One case is also compared with the oracle directly.
+status flag set. One case is also compared with the oracle directly.
 """
 import numpy as np
 import pytest
@@ -48,10 +48,11 @@ def _run_both(w):
     code = ext.EXTATTN_BF16 if w.dtype == "bf16" else ext.EXTATTN_F32
     ws = torch.zeros(ext.workspace_bytes(prefix, extend, w.n_q_heads, hkv, d, code), dtype=torch.uint8,
                      device="cuda")
-    ext.extend_attention_append(qd, kd, vd, fus.k, fus.v, fus.bt, prefix, extend, w.scale, o2, l2, workspace=ws)
-    torch.cuda.synchronize()
-    err = int(ws[:4].view(torch.int32).item())
-    return (o1, l1, sep), (o2, l2, fus), err, q
+    ext.extend_attention_append(qd, kd, vd, fus.k, fus.v, fus.bt, prefix, extend, w.scale, o2, l2, workspace=ws,
+                                check=False)
+    flags, _, exact = ext.read_status(ws)
+    assert exact == 0, f"{exact} waves took the exact path"
+    return (o1, l1, sep), (o2, l2, fus), flags, q
 
 
 @pytest.mark.parametrize("case", [
@@ -68,7 +69,7 @@ def test_fused_append_matches_separate(case):
                         mult=0.5 if dt == "bf16" else 1.0)
     log(f"fused append {launches} Hq={hq} Hkv={hkv} D={d} {dt}")
     (o1, l1, sep), (o2, l2, fus), err, q = _run_both(w)
-    assert err == 0, f"error word {err:#x}"
+    assert err == 0, f"status flags {err:#x}"
     assert torch.equal(_bits(sep.k), _bits(fus.k)), "K cache differs from kv_append's"
     assert torch.equal(_bits(sep.v), _bits(fus.v)), "V cache differs from kv_append's"
     assert torch.equal(o1, o2), "out differs from append + extend"
@@ -84,10 +85,11 @@ def test_fused_append_against_oracle():
     check_launch(w, o2, l2, {r.index: int(o) for r, o in zip(w.requests, offs)}, q, what="fused append")
 
 
-def test_fused_append_invalid_block_ids_are_counted_not_written():
+def test_fused_append_invalid_block_ids_are_reported_not_written():
     """A new token whose block id is out of range is neither written nor read
-    (the zero page stands in) and is counted in the error word; the other
-    blocks are written as kv_append writes them."""
+    (the zero page stands in) and is reported in the status words; the other
+    blocks are written as kv_append writes them. With the default check the
+    call raises, also with a workspace of its own."""
     w = custom_workload(781, [(40, 24)], 8, 8, 128)
     r = w.requests[0]
     fus = PagedCache(w, fill=0.0)
@@ -101,16 +103,20 @@ def test_fused_append_invalid_block_ids_are_counted_not_written():
     ws = torch.zeros(ext.workspace_bytes([40], [24], 8, 8, 128, ext.EXTATTN_BF16), dtype=torch.uint8,
                      device="cuda")
     before = fus.k.clone()
-    ext.extend_attention_append(q, kn, vn, fus.k, fus.v, bad, [40], [24], w.scale, out, None, workspace=ws)
-    torch.cuda.synchronize()
-    err = int(ws[:4].view(torch.int32).item())
-    assert err > 0 and not (err & (1 << 30)), f"error word {err:#x}"
+    ext.extend_attention_append(q, kn, vn, fus.k, fus.v, bad, [40], [24], w.scale, out, None, workspace=ws,
+                                check=False)
+    flags, count, _ = ext.read_status(ws)
+    assert flags == ext.STATUS_BAD_BLOCK and count > 0, f"status {flags:#x} / {count}"
     assert torch.isfinite(out.float()).all()
     blocks = [int(b) for b in r.blocks]
     # positions 40..47 (block 2) were written; nothing else changed
     assert not torch.equal(fus.k[blocks[2]], before[blocks[2]])
     others = [b for b in range(w.num_blocks) if b != blocks[2]]
     assert torch.equal(fus.k[others], before[others])
+    with pytest.raises(ValueError, match="block id outside"):
+        ext.extend_attention_append(q, kn, vn, fus.k, fus.v, bad, [40], [24], w.scale, out, None, workspace=ws)
+    with pytest.raises(ValueError, match="block id outside"):
+        ext.extend_attention_append(q, kn, vn, fus.k, fus.v, bad, [40], [24], w.scale, out, None)
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
