@@ -36,22 +36,34 @@ def _inputs(seed: int, n: int):
     return round_to_bf16(q)[0], round_to_bf16(k)[0], round_to_bf16(v)[0]
 
 
-@pytest.mark.parametrize("prefix,extend", [(0, 512), (960, 96)])
-def test_rising_scores_take_the_exact_path(prefix, extend):
+@pytest.mark.parametrize("prefix,extend,decode", [(0, 512, False), (960, 96, False), (960, 96, True)])
+def test_rising_scores_take_the_exact_path(prefix, extend, decode):
+    """decode=True adds a decode row (ordinary scores) to the launch, so the chunk rows
+    run in the mixed kernel instead of the chunk-only one."""
     n = prefix + extend
-    w = custom_workload(900 + prefix, [(prefix, extend)], HQ, HKV, D)
+    launches = [(prefix, extend)] + ([(300, 1)] if decode else [])
+    w = custom_workload(900 + prefix, launches, HQ, HKV, D)
     q, k, v = _inputs(31 + prefix, n)
-    log(f"rising scores: P={prefix}, E={extend}, {HQ}/{HKV} heads, D={D}")
+    log(f"rising scores: P={prefix}, E={extend}, {HQ}/{HKV} heads, D={D}, decode row: {decode}")
     cache = PagedCache(w)
     cache.expect_fast = False
     cache.append([0], [0], k, v, [n])
-    out, lse = cache.attend([0], [prefix], [extend], q[prefix:])
+    q_all = q[prefix:]
+    if decode:
+        r = w.requests[1]
+        cache.append([1], [0], w.k(r, 0, 301), w.v(r, 0, 301), [301])
+        q_all = np.concatenate([q_all, w.q(r, 300, 301)])
+    out, lse = cache.attend(list(range(len(launches))), [p for p, _ in launches], [e for _, e in launches], q_all)
     torch.cuda.synchronize()
     exact = ext.last_status()[2]
     log(f"  waves on the exact path: {exact}")
     assert exact > 0, "rising scores must push waves past the fast loop's bound"
     pos = np.arange(prefix, n)
     o_ref, lse_ref = oracle.attend_rows(q[prefix:], k, v, pos, w.scale)
+    if decode:
+        r = w.requests[1]
+        o_d, l_d = oracle.attend_rows(w.q(r, 300, 301), w.k(r, 0, 301), w.v(r, 0, 301), np.array([300]), w.scale)
+        o_ref, lse_ref = np.concatenate([o_ref, o_d]), np.concatenate([lse_ref, l_d])
     o = out.float().cpu().numpy().astype(np.float64)
     ls = lse.cpu().numpy().astype(np.float64)
     assert np.isfinite(o).all() and np.isfinite(ls).all()
