@@ -295,11 +295,11 @@ void attn_bf16_kernel(AttnArgs a) {
   }
   if (it.kind == kItemAppend) {
     append_item<D, kWaves>(a, it);
+  } else if (it.kind == kItemChunk) {
+    chunk_item_t<D, 1, kWaves>(a, it, smem);  // waits for the appends before its first new-key copy
   } else {
     if (a.n_append > 0 && it.key_end > a.seqs[it.seq].prefix) wait_appends<kWaves>(a);  // reads new keys
-    if (it.kind == kItemChunk)
-      chunk_item_t<D, 1, kWaves>(a, it, smem);
-    else if (it.nrows <= kSplitRows)
+    if (it.nrows <= kSplitRows)
       split_item<D, 1>(a, it, smem);
     else
       split_item<D, 2>(a, it, smem);

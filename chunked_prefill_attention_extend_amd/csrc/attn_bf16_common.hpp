@@ -186,12 +186,12 @@ __device__ void append_item(const AttnArgs& a, const WorkItem& it) {
 
 constexpr int kWaitSpinLimit = 1 << 20;  // polls, ~0.3 us apart: ~0.3 s
 
-// One lane polls the counter (relaxed, spaced out so that hundreds of waiting
-// workgroups do not flood one address), then one acquire fence makes the appended
-// K/V visible before the workgroup's first load.
+// Lane 0 of the calling wave polls the counter until every append wave is done
+// (relaxed loads spaced out, so that hundreds of waiting waves do not flood one
+// address; bounded, leaving kStatusWaitTimeout if it gives up).
 template <int WAVES>
-__device__ void wait_appends(const AttnArgs& a) {
-  if (threadIdx.x == 0) {
+__device__ inline void poll_appends(const AttnArgs& a) {
+  if ((threadIdx.x & 63) == 0) {
     const int target = a.n_append * WAVES;
     int spins = 0;
     while (__hip_atomic_load(a.append_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
@@ -201,9 +201,26 @@ __device__ void wait_appends(const AttnArgs& a) {
         break;
       }
     }
+  }
+}
+
+// The whole workgroup waits: one lane polls, then one acquire fence makes the
+// appended K/V visible before the workgroup's first load.
+template <int WAVES>
+__device__ void wait_appends(const AttnArgs& a) {
+  if (threadIdx.x == 0) {
+    poll_appends<WAVES>(a);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
+}
+
+// One wave waits (for its own later loads): its lane 0 polls, then the wave's
+// acquire fence.
+template <int WAVES>
+__device__ void wait_appends_wave(const AttnArgs& a) {
+  poll_appends<WAVES>(a);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 }  // namespace extattn

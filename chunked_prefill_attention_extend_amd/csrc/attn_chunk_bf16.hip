@@ -20,8 +20,7 @@ void chunk_bf16_kernel(AttnArgs a) {
   if (it.kind == kItemAppend) {
     append_item<D, WAVES>(a, it);
   } else {
-    if (a.n_append > 0 && it.key_end > a.seqs[it.seq].prefix) wait_appends<WAVES>(a);  // reads new keys
-    chunk_item_t<D, RB, WAVES>(a, it, smem);
+    chunk_item_t<D, RB, WAVES>(a, it, smem);  // waits for the appends before its first new-key copy
   }
   if (a.stamps) {
     __syncthreads();

@@ -360,6 +360,13 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
     }
   };
 
+  // Fused append: the launch's append items write the new tokens' K/V (keys P and
+  // up) into the cache. Tiles below tile P / 32 hold only older keys, in whole cache
+  // blocks the appends never touch, so a wave waits for the appends only before it
+  // copies tile P / 32 (relative index v_new), if that tile is in its range.
+  const int v_new = (si.prefix >> 5) - t0;
+  const bool wait_new = a.n_append > 0 && v_new < n;
+
   if (n > 0) {
     constexpr int kIssuePerStep = 2 * NINST;
     // Prologue: ids of windows 0 and 1; K of tiles t0 .. t0+KLEAD-1 and V of t0 ..
@@ -368,6 +375,7 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
     fill_ids(1);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     make_entries(0, -1);
+    if (wait_new && v_new < KLEAD) wait_appends_wave<WAVES>(a);
 #pragma unroll
     for (int v = 0; v < KLEAD; ++v) issue_k(v, v);
 #pragma unroll
@@ -426,6 +434,7 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
         if ((u & 31) == 0 && u > 0) fill_ids((u >> 5) + 1);
       }
       auto issue = [&]() {
+        if (wait_new && u + KLEAD == v_new) wait_appends_wave<WAVES>(a);  // first copy of a new-key tile
         issue_k(u + KLEAD, (sl + KLEAD) % RING);
         issue_v(u + VLEAD, (sl + VLEAD) % RING);
       };

@@ -29,8 +29,10 @@ def test_prompt4000_all_chunks_all_rows():
 
 
 def test_prefix_cache32k_sampled_rows():
-    log("prefix_cache32k: 2 chunks at P=16384/24576, sampled rows")
-    res = run_planned(make_workload("prefix_cache32k"), rows_per_chunk=48)
+    """Both chunks, rows {0, 1, E/2, E-2, E-1} and 251 seeded random rows each, all
+    32 heads (the 128-chunk sweep has its own module, test_sweep_parity_gpu.py)."""
+    log("prefix_cache32k: 2 chunks at P=16384/24576, 256 sampled rows each")
+    res = run_planned(make_workload("prefix_cache32k"), rows_per_chunk=256)
     assert len(res) == 2
 
 
@@ -41,12 +43,6 @@ def test_mixed_budget2048():
     rng = np.random.default_rng(3)
     chunk_rows = np.unique(np.concatenate([[0, 1, 991, 1982, 1983], rng.choice(1984, 120, replace=False)]))
     check_launch(w, out, lse, q_off, q, row_sample={64: chunk_rows}, what="mixed step")
-
-
-def test_sweep128k_sampled_chunks():
-    log("sweep128k: 128 chunks appended, chunks 0, 1, 64, 127 compared on sampled rows")
-    res = run_planned(make_workload("sweep128k"), check_chunks=[0, 1, 64, 127], rows_per_chunk=12)
-    assert len(res) == 4
 
 
 @pytest.mark.parametrize("case", [
