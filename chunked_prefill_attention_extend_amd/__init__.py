@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     decode_first_with_slack,
     extend_attention,
     extend_attention_append,
+    extend_attention_noalloc,
     kv_append,
     last_status,
     load_library,

@@ -83,6 +83,8 @@ def load_library() -> ctypes.CDLL:
     lib.extattn_plan_cache_stats.argtypes = [_c_i64p, _c_i64p, _c_i32p, _c_i64p]
     lib.extattn_plan_cache_clear.restype = ctypes.c_int
     lib.extattn_plan_cache_clear.argtypes = []
+    lib.extattn_extend_attention_noalloc.restype = ctypes.c_int
+    lib.extattn_extend_attention_noalloc.argtypes = [*lib.extattn_extend_attention.argtypes[:17], ctypes.c_void_p]
     lib.extattn_read_status.restype = ctypes.c_int
     lib.extattn_read_status.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32), _c_i32p, _c_i32p,
                                         ctypes.c_void_p]
@@ -118,11 +120,13 @@ _last_status = (0, 0, 0)
 
 def read_status(workspace, stream=None) -> tuple[int, int, int]:
     """``(flags, bad_block_reads, exact_waves)`` left in ``workspace`` by the last
-    call that used it (waits for ``stream``, default torch's current stream)."""
+    call that used it (waits for ``stream``, default torch's current stream);
+    ``workspace=None`` reads the allocation-free entry point's scratch."""
     global _last_status
     flags, count, exact = ctypes.c_uint32(0), ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(load_library().extattn_read_status(workspace.data_ptr(), ctypes.byref(flags), ctypes.byref(count),
-                                              ctypes.byref(exact), _stream_handle(stream)))
+    ws = workspace.data_ptr() if workspace is not None else None
+    _check(load_library().extattn_read_status(ws, ctypes.byref(flags), ctypes.byref(count), ctypes.byref(exact),
+                                              _stream_handle(stream)))
     _last_status = (flags.value, count.value, exact.value)
     return _last_status
 
@@ -358,6 +362,9 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, prefix_lens, extend_l
         _raise_on_status(ws, stream, "kv_append")
 
 
+_NO_WORKSPACE = object()  # marks the allocation-free call in _extend_args
+
+
 def _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale, out, lse, workspace, stream):
     """Checks shared by the extend-attention entry points; returns (lib, p, e, hkv, d, ws, args).
     The caller holds ``ws`` (the workspace, maybe allocated here) until its launches are enqueued."""
@@ -379,7 +386,9 @@ def _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, sca
                             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [sum(E), Hq] tensor")
     code = _dtype_code(q)
-    if workspace is None:
+    if workspace is _NO_WORKSPACE:  # the allocation-free entry point: nothing is allocated here either
+        ws = None
+    elif workspace is None:
         ws = _workspace(workspace_bytes(p, e, hq, hkv, d, code), q.device, None, stream)
     else:  # the library checks the size itself (EXTATTN_ENOSPC): no second planning pass here
         if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or not workspace.is_cuda:
@@ -387,8 +396,8 @@ def _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, sca
         ws = workspace
     args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1], nb,
             _ptr(p), _ptr(e), len(p), hq, hkv, d, bs, float(scale), code, out.data_ptr(),
-            lse.data_ptr() if lse is not None else None, ws.data_ptr(), ws.numel() * ws.element_size(),
-            _stream_handle(stream))
+            lse.data_ptr() if lse is not None else None, ws.data_ptr() if ws is not None else None,
+            ws.numel() * ws.element_size() if ws is not None else 0, _stream_handle(stream))
     return lib, p, e, hkv, d, ws, args
 
 
@@ -448,4 +457,17 @@ def extend_attention_append(q, k_new, v_new, k_cache, v_cache, block_table, pref
     _check(lib.extattn_extend_attention_append(args[0], k_new.data_ptr(), v_new.data_ptr(), *args[1:]))
     if check:
         _raise_on_status(ws, stream, "extend_attention_append")
+    return out
+
+
+def extend_attention_noalloc(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale: float, out,
+                             lse=None, stream=None, check: bool = False):
+    """``extend_attention`` through the allocation-free entry point: the library's
+    static 64 MiB device scratch is the workspace, so nothing is allocated (calls on
+    one GPU share it and must not overlap). Returns ``out``."""
+    lib, p, e, _, _, ws, args = _extend_args(q, k_cache, v_cache, block_table, prefix_lens, extend_lens, scale,
+                                             out, lse, _NO_WORKSPACE, stream)
+    _check(lib.extattn_extend_attention_noalloc(*args[:17], args[19]))
+    if check:
+        _raise_on_status(None, stream, "extend_attention_noalloc")
     return out

@@ -171,13 +171,24 @@ int check_blocks(int32_t num_seqs, const int32_t* prefix, const int32_t* extend,
 
 }  // namespace
 
+namespace extattn {
+int set_error(int code, const char* msg) { return fail(code, msg); }
+int set_hip_error(hipError_t e, const char* what) { return hip_fail(e, what); }
+}  // namespace extattn
+
 extern "C" {
 
 const char* extattn_last_error(void) { return g_error.c_str(); }
 
 int extattn_read_status(const void* workspace, uint32_t* flags, int32_t* bad_block_reads, int32_t* exact_waves,
                         void* stream) {
-  if (!workspace || !flags || !bad_block_reads || !exact_waves) return fail(EXTATTN_EINVAL, "null pointer");
+  if (!flags || !bad_block_reads || !exact_waves) return fail(EXTATTN_EINVAL, "null pointer");
+  if (!workspace) {  // the allocation-free entry point's scratch on the current device
+    void* p = nullptr;
+    const int rc = noalloc_scratch(&p);
+    if (rc != EXTATTN_OK) return rc;
+    workspace = p;
+  }
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(EXTATTN_EINVAL, "workspace must be 256-byte aligned");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   int32_t words[3] = {0, 0, 0};
@@ -332,7 +343,7 @@ int extattn_kv_append(const void* k_new, const void* v_new, void* k_cache, void*
 
 }  // extern "C"
 
-namespace {
+namespace extattn {
 
 // Checks, planning, metadata upload and launches of one extend-attention call;
 // with `timed`, the attention kernel records per-item wall-clock stamps.
@@ -341,7 +352,7 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                 int32_t block_size, float scale, int32_t dtype, void* out, float* lse, void* workspace,
                 size_t workspace_bytes, void* stream, bool timed, int64_t* stamps, int32_t capacity,
-                int32_t* n_items, double* tick_hz, const void* k_new = nullptr, const void* v_new = nullptr) {
+                int32_t* n_items, double* tick_hz, const void* k_new, const void* v_new, MetaUploader upload_fn) {
   const bool fused = k_new != nullptr || v_new != nullptr;
   int rc = check_common(num_seqs, prefix_lens, extend_lens, num_q_heads, num_kv_heads, head_dim, dtype, true);
   if (rc != EXTATTN_OK) return rc;
@@ -357,7 +368,9 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
   if (rc != EXTATTN_OK)
     return fail(rc, rc == EXTATTN_ENOSPC ? "launch too large: partial results exceed 2^31 floats" : "planning failed");
   const Plan& plan = lp->plan;
-  if (workspace_bytes < plan.bytes) return fail(EXTATTN_ENOSPC, "workspace too small");
+  if (workspace_bytes < plan.bytes)
+    return fail(EXTATTN_ENOSPC, "workspace too small: the launch needs " + std::to_string(plan.bytes) + " bytes, " +
+                                    std::to_string(workspace_bytes) + " available");
   // the plan lists the fused append's items first; a plain launch starts after them
   const int32_t first = fused ? 0 : plan.n_append;
   const int32_t n_launch = int32_t(plan.items.size()) - first;
@@ -375,7 +388,7 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
   }
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  rc = upload(lp->blob.data(), lp->blob.size(), workspace, st);
+  rc = upload_fn ? upload_fn(*lp, workspace, st) : upload(lp->blob.data(), lp->blob.size(), workspace, st);
   if (rc != EXTATTN_OK) return rc;
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -452,7 +465,7 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
   return EXTATTN_OK;
 }
 
-}  // namespace
+}  // namespace extattn
 
 extern "C" {
 

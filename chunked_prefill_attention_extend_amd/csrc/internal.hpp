@@ -173,6 +173,24 @@ int make_launch_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* ext
 int get_launch_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, int32_t hq, int32_t hkv,
                     int32_t head_dim, int32_t dtype, std::shared_ptr<const LaunchPlan>& out);
 void plan_cache_configure(int32_t max_entries, int64_t max_bytes);
+
+// api.cpp: one extend-attention call (checks, plan, metadata upload, launches).
+// `upload` copies the plan's metadata into the workspace on the stream; nullptr
+// uses the library's pinned staging pool and copies the whole image.
+using MetaUploader = int (*)(const LaunchPlan& lp, void* workspace, hipStream_t stream);
+int extend_call(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                int32_t max_blocks, int64_t num_blocks, const int32_t* prefix_lens, const int32_t* extend_lens,
+                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                int32_t block_size, float scale, int32_t dtype, void* out, float* lse, void* workspace,
+                size_t workspace_bytes, void* stream, bool timed, int64_t* stamps, int32_t capacity,
+                int32_t* n_items, double* tick_hz, const void* k_new = nullptr, const void* v_new = nullptr,
+                MetaUploader upload = nullptr);
+int set_error(int code, const char* msg);           // thread-local message, returns code
+int set_hip_error(hipError_t e, const char* what);  // returns EXTATTN_EHIP
+
+// noalloc.hip: the allocation-free entry point's static device scratch.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+int noalloc_scratch(void** ptr);  // this device's scratch address (looked up once per device)
 void plan_cache_stats(int64_t* hits, int64_t* misses, int32_t* entries, int64_t* bytes);
 void plan_cache_clear();
 

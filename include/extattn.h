@@ -345,13 +345,40 @@ int extattn_extend_attention_timed(const void* q, const void* k_cache, const voi
                                    double* tick_hz);
 
 /*
+ * Extend attention that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). The same computation, kernels and results as
+ * extattn_extend_attention; the workspace is a static device scratch of 64 MiB
+ * inside the library (each GPU the library runs on holds one until the process
+ * ends), and the call's metadata reaches it through kernel arguments, so no
+ * pinned staging is used either.
+ *
+ * Arguments, ownership and errors as for extattn_extend_attention, without
+ * workspace / workspace_bytes; EXTATTN_ENOSPC when the launch needs more than the
+ * 64 MiB scratch (extattn_workspace_bytes gives the need; partial results of
+ * key-range pieces are the bulk of it).
+ * All calls on one GPU share its scratch, which keeps the last call's contents:
+ * calls that overlap on one GPU (several streams or threads) race and must be
+ * serialised by the caller. The status words of the last call on the current
+ * device are read with extattn_read_status(NULL, ...).
+ */
+int extattn_extend_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table, int32_t max_blocks, int64_t num_blocks,
+                                     const int32_t* prefix_lens, const int32_t* extend_lens, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, float scale, int32_t dtype, void* out, float* lse,
+                                     void* stream);
+
+/*
  * Status of the last call that used `workspace` (any call taking a workspace:
  * extattn_kv_append, extattn_extend_attention and its _append / _timed
  * variants). The msmodeling chunked-prefill RFC, section 2.4 (reliability:
  * invalid input is reported at the entry with a clear error, never swallowed),
  * asks for this for the checks that only the GPU can make.
  *
- * Enqueues a copy of the workspace's two status words on `stream`, then waits
+ * workspace NULL reads the scratch of extattn_extend_attention_noalloc on the
+ * current device.
+ * Enqueues a copy of the workspace's status words on `stream`, then waits
  * on the host until the stream has completed it (hipStreamSynchronize): call
  * it where a host wait is acceptable (tests, a periodic health check, after a
  * fused-append call whose results matter).
@@ -363,7 +390,7 @@ int extattn_extend_attention_timed(const void* q, const void* k_cache, const voi
  *                   past 2^64 against the first tile's row max (scores rising by
  *                   more than 64 in log2 units along the keys). Informational:
  *                   the results are valid; the count shows where time went.
- * Errors: EXTATTN_EINVAL for null pointers or a workspace not 256-byte
+ * Errors: EXTATTN_EINVAL for null output pointers or a workspace not 256-byte
  * aligned; EXTATTN_EHIP if the copy or the wait fails.
  */
 int extattn_read_status(const void* workspace, uint32_t* flags, int32_t* bad_block_reads, int32_t* exact_waves,
