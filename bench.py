@@ -156,9 +156,15 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
     out = torch.empty_like(q)
     lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=dev)
     bt = torch.from_numpy(bt_all).to(dev)
-    ws = torch.empty(ext.workspace_bytes(prefix, extend, hq, hkv, d, ext.EXTATTN_BF16), dtype=torch.uint8,
-                     device=dev)
     dec = [i for i, r in enumerate(reqs) if r.launch[1] == 1]
+    ci = [i for i in range(len(reqs)) if i not in dec]
+    # one workspace for the three launches timed below (the whole step, its decode
+    # rows alone, its chunk alone)
+    ws_bytes = max(ext.workspace_bytes(prefix, extend, hq, hkv, d, ext.EXTATTN_BF16),
+                   ext.workspace_bytes([prefix[i] for i in dec], [1] * len(dec), hq, hkv, d, ext.EXTATTN_BF16),
+                   ext.workspace_bytes([prefix[i] for i in ci], [extend[i] for i in ci], hq, hkv, d,
+                                       ext.EXTATTN_BF16))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     bt_dec = torch.from_numpy(bt_all[dec]).to(dev)
     q_dec = q[:len(dec)] if dec == list(range(len(dec))) else None
     assert q_dec is not None, "decode rows are expected first"
@@ -189,7 +195,6 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
                                                workspace=ws))
     (t_dec, t_dec_min) = timed(lambda: ext.extend_attention(q_dec, k_cache, v_cache, bt_dec, [prefix[i] for i in dec],
                                                [1] * len(dec), w.scale, out_dec, lse_dec, workspace=ws))
-    ci = [i for i in range(len(reqs)) if i not in dec]
     c_off = sum(extend[i] for i in dec)   # the chunk's rows follow the decode rows
     q_chk = q[c_off:]
     out_chk = torch.empty_like(q_chk)

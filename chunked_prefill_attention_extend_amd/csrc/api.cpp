@@ -37,13 +37,16 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 // Pinned host staging for the metadata copied into the caller's workspace.
-// Each device has a pool of pinned buffers; a buffer is reused only after the
-// copy that last read it has completed (an event per buffer). A call takes a
-// free buffer, or adds one to the pool, so it does not wait for the GPU; only
-// when kMaxStaging buffers are in flight on the device does it wait (on the
+// Each device has a pool of pinned, coherent, device-mapped buffers; a copy kernel
+// on the caller's stream reads a buffer over the host link (a DMA-engine copy would
+// make the next kernel wait for a cross-engine signal). A buffer is reused only
+// after the copy that last read it has completed (an event per buffer). A call
+// takes a free buffer, or adds one to the pool, so it does not wait for the GPU;
+// only when kMaxStaging buffers are in flight on the device does it wait (on the
 // host, outside the pool's lock) for the oldest of them.
 struct StagingSlot {
   void* host = nullptr;
+  void* dev = nullptr;  // the same buffer's device address
   size_t cap = 0;
   hipEvent_t done = nullptr;
 };
@@ -112,19 +115,27 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   if (s->cap < bytes) {
     if (s->host) (void)hipHostFree(s->host);
     s->host = nullptr;
+    s->dev = nullptr;
     s->cap = 0;
     size_t cap = kStagingMinBytes;
     while (cap < bytes) cap *= 2;
-    e = hipHostMalloc(&s->host, cap, hipHostMallocDefault);
+    e = hipHostMalloc(&s->host, cap, hipHostMallocMapped | hipHostMallocCoherent);
     if (e != hipSuccess) {
       s->host = nullptr;
       return give_back(hip_fail(e, "hipHostMalloc (staging)"));
     }
+    e = hipHostGetDevicePointer(&s->dev, s->host, 0);
+    if (e != hipSuccess || !s->dev) {
+      (void)hipHostFree(s->host);
+      s->host = nullptr;
+      s->dev = nullptr;
+      return give_back(hip_fail(e != hipSuccess ? e : hipErrorInvalidValue, "hipHostGetDevicePointer (staging)"));
+    }
     s->cap = cap;
   }
   std::memcpy(s->host, src, bytes);
-  e = hipMemcpyAsync(dst, s->host, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return give_back(hip_fail(e, "hipMemcpyAsync (metadata)"));
+  e = launch_meta_copy(s->dev, dst, bytes, stream);
+  if (e != hipSuccess) return give_back(hip_fail(e, "metadata copy launch"));
   e = hipEventRecord(s->done, stream);
   if (e != hipSuccess) {
     // the copy may still read the buffer: keep it out of the pool

@@ -215,5 +215,8 @@ hipError_t launch_chunk_bf16(const AttnArgs& a, hipStream_t stream);  // chunk a
 hipError_t launch_combine(const AttnArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const KvArgs& a, int32_t dtype, hipStream_t stream);
+// Copies `bytes` from `src` (pinned host memory mapped into the device, 16-byte
+// aligned) to device memory `dst` with a kernel on `stream`.
+hipError_t launch_meta_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 }  // namespace extattn
