@@ -93,6 +93,7 @@ def test_token_budget_invariants():
 
 def test_mixed_chunk_invariants():
     rng = random.Random(12)
+    unaligned_continuations = 0
     for _ in range(3000):
         decode = [rng.randrange(0, 9000) for _ in range(rng.randrange(0, 40))]
         chunked = None
@@ -111,11 +112,17 @@ def test_mixed_chunk_invariants():
         assert sum(e[3] for e in pre) + left == budget and left >= 0
         if chunked is not None and pre:
             assert pre[0][0] == "chunked" and pre[0][2] == chunked[1]
+        if chunked is not None:
+            # a continuation takes min(budget, rest of the request), page aligned or not
+            take = min(budget, chunked[0] - chunked[1])
+            assert [e[3] for e in pre if e[0] == "chunked"] == ([take] if take > 0 else [])
+            unaligned_continuations += page > 1 and take % page != 0
         cut = [e for e in pre if e[0] == "waiting" and e[3] < waiting[e[1]][0] - waiting[e[1]][1]]
         assert len(cut) <= 1
         if cut:  # a first cut ends on a page boundary and is the last entry
             assert (cut[0][2] + cut[0][3]) % page == 0 and cut[0] == pre[-1]
             assert nc == ("waiting", cut[0][1], waiting[cut[0][1]][0], cut[0][2] + cut[0][3])
+    assert unaligned_continuations > 100  # the branch the goldens with page_size > 1 pin
 
 
 def test_decode_first_invariants():
