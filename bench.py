@@ -11,10 +11,15 @@ step time, with all inputs resident in HBM before the timed region.
 The JSON line also carries:
 * roofline: the attention kernel's achieved TFLOP/s over its own launches
   (HIP events on the launch stream around every extend_attention call),
-  against the bf16 dense MFMA peak;
+  against the bf16 dense MFMA peak, with the shader clock the kernel ran at
+  (measured from one timed launch's per-workgroup cycle and wall-clock stamps);
 * mixed_step: the 2048-token mixed step (64 decode rows + a 1984-row chunk in
   one launch); decode-row HBM GB/s measured on the same launch with the chunk
   request removed, against the 8 TB/s HBM peak;
+* verify_rows: multi-token verify rows (E = 1..8) over the mixed step's contexts;
+* config_table: GPU time of the three single-prompt workloads (tiny fp32, a
+  4000-token prompt, 32768 tokens at hit rate 0.5);
+* chunk_size_sweep: attention TFLOP/s of one 65536-token prompt at C = 256 .. 16384;
 * cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -35,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4 SIMD x 1024 bf16 FLOP/clk x 2.4 GHz (dense)
+PEAK_CLOCK_GHZ = 2.4
 PEAK_HBM_GBS = 8000.0
 
 SWEEP = dict(n=131072, chunk=1024, hq=64, hkv=8, d=128)
@@ -44,7 +50,8 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_sweep128k_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_bf16_sweep128k_traffic.json")
+SWEEP_KERNEL = "chunk_bf16_kernel<128, 1, 8>"   # the attention kernel of the sweep's launches
 
 
 def code_hash(files) -> str:
@@ -121,6 +128,19 @@ def sweep_step(ext, s, events=None, fused=False):
                              s["out"][p:p + e], s["lse"][p:p + e], workspace=s["ws"])
         if events is not None:
             events[t][1].record()
+
+
+def shader_clock(torch, ext, s, t: int = -1):
+    """The shader clock the attention kernel runs at on sweep chunk t (the last,
+    heaviest one by default): a timed launch of that chunk, whose per-workgroup
+    stamps hold both shader-clock cycles and wall-clock ticks. Returns GHz, the
+    cycle-weighted mean over the workgroups."""
+    p, e = s["plan"][t]
+    _, st, hz = ext.extend_attention(s["q"][p:p + e], s["k_cache"], s["v_cache"], s["bt"], [p], [e], s["scale"],
+                                     s["out"][p:p + e], s["lse"][p:p + e], workspace=s["ws"], timed=True)
+    torch.cuda.synchronize()
+    st = st.cpu().numpy().astype(np.float64)
+    return float((st[:, 5] - st[:, 4]).sum() / ((st[:, 1] - st[:, 0]).sum() / hz) / 1e9)
 
 
 def check_status(ext, s) -> None:
@@ -217,8 +237,9 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
         st = st.cpu().numpy()
         dsel, csel = st[:, 2] == 1, st[:, 2] == 0
         spans.append(((st[dsel, 1].max() - st[dsel, 0].min()) / hz, (st[csel, 1].max() - st[csel, 0].min()) / hz,
-                      (st[:, 1].max() - st[:, 0].min()) / hz))
-    dspan, cspan, kspan = (float(np.median([x[j] for x in spans])) for j in range(3))
+                      (st[:, 1].max() - st[:, 0].min()) / hz,
+                      float((st[:, 5] - st[:, 4]).sum() / ((st[:, 1] - st[:, 0]).sum() / hz) / 1e9)))
+    dspan, cspan, kspan, sclk = (float(np.median([x[j] for x in spans])) for j in range(4))
     chunk = [(p, e) for p, e in zip(prefix, extend) if e > 1]
     chunk_flops = sweep_flops(chunk, hq, d)
     return {
@@ -238,6 +259,7 @@ def mixed_step_bench(torch, ext, synth, reps: int = 10):
         "chunk_span_in_mixed_ms": cspan * 1e3,
         "attention_kernel_span_ms": kspan * 1e3,
         "span_note": "per-workgroup wall-clock stamps (measurement variant of the same launch), median of %d" % reps,
+        "sclk_ghz_in_mixed": sclk,
         "chunk_flops": chunk_flops,
         "ms_chunk_rows_only": t_chk * 1e3,
         "chunk_tflops_alone": chunk_flops / t_chk / 1e12,
@@ -410,12 +432,12 @@ def chunk_size_sweep(torch, ext, synth, n: int = 65536, sizes=(256, 512, 1024, 2
             "flops": sweep_flops(ext.chunk_plan(n, sizes[0], 0.0)["chunks"], hq, d), "rows": rows}
 
 
-def config_table(torch, ext, synth, reps: int = 5):
+def config_table(torch, ext, synth, reps: int = 5, compact: bool = False):
     """GPU time of the pages' single-prompt workloads (tiny fp32 64 tokens at C=16;
     a 4000-token prompt at C=512; 32768 tokens at hit rate 0.5 and C=8192): each
     planned chunk's K/V is appended, then its extend launch is timed with HIP
     events (median of reps). The mixed step and the 128k sweep are the default
-    bench lines."""
+    bench lines. ``compact`` leaves out the per-chunk rows."""
     out = []
     for name in ("tiny_f32", "prompt4000", "prefix_cache32k"):
         w = synth.make_workload(name)
@@ -452,8 +474,11 @@ def config_table(torch, ext, synth, reps: int = 5):
             chunks.append({"prefix": p_, "extend": e_, "ms": t * 1e3, "tflops": f / t / 1e12})
         tot_f = sum(sweep_flops([(x["prefix"], x["extend"])], hq, d) for x in chunks)
         tot_t = sum(x["ms"] for x in chunks) * 1e-3
-        out.append({"workload": name, "dtype": w.dtype, "chunks": chunks, "flops": tot_f,
-                    "attention_ms": tot_t * 1e3, "tflops": tot_f / tot_t / 1e12})
+        row = {"workload": name, "dtype": w.dtype, "n_chunks": len(chunks), "flops": tot_f,
+               "attention_ms": tot_t * 1e3, "tflops": tot_f / tot_t / 1e12}
+        if not compact:
+            row["chunks"] = chunks
+        out.append(row)
         log(f"{name}: {len(chunks)} chunks, {tot_t * 1e3:.3f} ms, {tot_f / tot_t / 1e12:.1f} TFLOP/s")
     return out
 
@@ -550,6 +575,7 @@ def main() -> int:
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--only-mixed", action="store_true", help="run only the mixed-step measurement (for profiling)")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused append + attention steps")
+    ap.add_argument("--no-tables", action="store_true", help="skip the config table and the chunk-size sweep")
     ap.add_argument("--config-table", action="store_true",
                     help="only time the pages' smaller workloads on the GPU and the oracle on all five")
     ap.add_argument("--chunk-sweep", action="store_true",
@@ -642,6 +668,9 @@ def main() -> int:
                  "note": "128 x extend_attention_append (append inside the attention launch)"}
         log(f"fused steps: {dtf / args.steps * 1e3:.1f} ms per step")
 
+    sclk = shader_clock(torch, ext, s)
+    log(f"shader clock on the last chunk: {sclk:.3f} GHz")
+
     mixed = None
     if not args.no_mixed:
         log("mixed step")
@@ -650,6 +679,12 @@ def main() -> int:
     if not args.no_mixed:
         log("verify rows")
         verify = verify_rows_sweep(torch, ext, synth)
+    configs = chunk_sizes = None
+    if not args.no_tables:
+        log("config table")
+        configs = config_table(torch, ext, synth, compact=True)
+        log("chunk-size sweep")
+        chunk_sizes = chunk_size_sweep(torch, ext, synth)
     log("calibration")
     calib = calibration(torch)
     planning = host_planning(ext, synth)
@@ -676,8 +711,13 @@ def main() -> int:
                    "flops_per_step": flops, "chunks": nchunk},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
-                     "kernel": "attn_bf16_kernel<128>",
-                     "avg_launch_ms": per_launch_s * 1e3, "flops_per_launch": flops / nchunk},
+                     "kernel": SWEEP_KERNEL,
+                     "avg_launch_ms": per_launch_s * 1e3, "flops_per_launch": flops / nchunk,
+                     "peak_clock_ghz": PEAK_CLOCK_GHZ, "sclk_ghz_measured": sclk,
+                     "peak_at_measured_clock": PEAK_BF16_TFLOPS * sclk / PEAK_CLOCK_GHZ,
+                     "clock_note": "peak = 256 CU x 4 SIMD x 1024 bf16 FLOP/clk at 2.4 GHz; sclk_ghz_measured: "
+                                   "shader-clock cycles / wall-clock time of the workgroups of one timed launch "
+                                   "of the last chunk"},
         "sweep_attention": {"aggregate_tflops": aggregate, "per_chunk_tflops": per_chunk,
                             "note": "attention launches only (kv_append excluded); sum(F) / sum(per-chunk median)"},
         "calibration": calib,
@@ -685,6 +725,8 @@ def main() -> int:
         "fused_append_step": fused,
         "mixed_step": mixed,
         "verify_rows": verify,
+        "config_table": configs,
+        "chunk_size_sweep": chunk_sizes,
         "cpu_baseline": base,
     }
     print(json.dumps(line), flush=True)

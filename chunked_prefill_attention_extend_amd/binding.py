@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libextattn.so")
 EXTATTN_OK, EXTATTN_EINVAL, EXTATTN_ENOSPC, EXTATTN_EUNSUPPORTED, EXTATTN_EHIP = 0, -1, -2, -3, -4
 EXTATTN_BF16, EXTATTN_F32 = 0, 1
 STATUS_BAD_BLOCK, STATUS_WAIT_TIMEOUT = 1, 2
+STAMP_WORDS = 6  # per work item of a timed launch: start, end, kind, request, clk_start, clk_end
 BLOCK_SIZE = 16
 
 _lib = None
@@ -408,8 +409,9 @@ def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens,
     q, out: device ``[sum(E), Hq, D]``; lse: device float32 ``[sum(E), Hq]`` or None;
     prefix_lens / extend_lens: host, one entry per block_table row.
     Returns ``out``; with ``timed`` (bf16 only) the measurement variant runs and
-    ``(out, stamps, tick_hz)`` is returned, ``stamps`` a device int64 ``[items, 4]``
-    of {start, end, kind (0 chunk, 1 decode / verify), request} per work item.
+    ``(out, stamps, tick_hz)`` is returned, ``stamps`` a device int64 ``[items, 6]``
+    of {start, end, kind (0 chunk, 1 decode / verify), request, clk_start, clk_end}
+    per work item (start / end in wall-clock ticks, clk in shader-clock cycles).
     With ``check`` the call waits for the stream and raises if the launch met a
     block id outside ``[0, num_blocks)`` (``ValueError``). Without it the status
     stays in the workspace (``read_status``); a workspace allocated here is
@@ -429,7 +431,7 @@ def extend_attention(q, k_cache, v_cache, block_table, prefix_lens, extend_lens,
     if rc != EXTATTN_ENOSPC or n.value < 1:
         _check(rc)
         raise RuntimeError("timed launch: no work items")
-    stamps = torch.empty((n.value, 4), dtype=torch.int64, device=q.device)
+    stamps = torch.empty((n.value, STAMP_WORDS), dtype=torch.int64, device=q.device)
     _check(lib.extattn_extend_attention_timed(*args, stamps.data_ptr(), n.value, ctypes.byref(n), ctypes.byref(hz)))
     if check:
         _raise_on_status(ws, stream, "extend_attention (timed)")

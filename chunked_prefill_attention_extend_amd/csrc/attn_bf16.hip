@@ -288,8 +288,9 @@ void attn_bf16_kernel(AttnArgs a) {
   // measurement variant: the workgroup's start and end (after its last wave) in
   // wall-clock ticks; the start is stored at once so that nothing stays live
   if (a.stamps && threadIdx.x == 0) {
-    int64_t* st = a.stamps + 4 * int64_t(blockIdx.x);
+    int64_t* st = a.stamps + kStampWords * int64_t(blockIdx.x);
     st[0] = int64_t(wall_clock64());
+    st[4] = int64_t(clock64());
     st[2] = it.kind;
     st[3] = it.seq;
   }
@@ -306,7 +307,11 @@ void attn_bf16_kernel(AttnArgs a) {
   }
   if (a.stamps) {
     __syncthreads();
-    if (threadIdx.x == 0) a.stamps[4 * int64_t(blockIdx.x) + 1] = int64_t(wall_clock64());
+    if (threadIdx.x == 0) {
+      int64_t* st = a.stamps + kStampWords * int64_t(blockIdx.x);
+      st[5] = int64_t(clock64());
+      st[1] = int64_t(wall_clock64());
+    }
   }
 }
 

@@ -12,8 +12,9 @@ void chunk_bf16_kernel(AttnArgs a) {
   const WorkItem it = a.items[blockIdx.x];
   // measurement variant: the workgroup's start and end in wall-clock ticks
   if (a.stamps && threadIdx.x == 0) {
-    int64_t* st = a.stamps + 4 * int64_t(blockIdx.x);
+    int64_t* st = a.stamps + kStampWords * int64_t(blockIdx.x);
     st[0] = int64_t(wall_clock64());
+    st[4] = int64_t(clock64());
     st[2] = it.kind;
     st[3] = it.seq;
   }
@@ -24,7 +25,11 @@ void chunk_bf16_kernel(AttnArgs a) {
   }
   if (a.stamps) {
     __syncthreads();
-    if (threadIdx.x == 0) a.stamps[4 * int64_t(blockIdx.x) + 1] = int64_t(wall_clock64());
+    if (threadIdx.x == 0) {
+      int64_t* st = a.stamps + kStampWords * int64_t(blockIdx.x);
+      st[5] = int64_t(clock64());
+      st[1] = int64_t(wall_clock64());
+    }
   }
 }
 

@@ -42,6 +42,10 @@ enum : int32_t {
   kItemAppend = 2, // fused append: copy new tokens [row0, row0 + nrows) of a request into the cache
 };
 
+// Measurement variant: one record per work item, {start, end} in wall-clock ticks,
+// {kind, request}, {start, end} in shader-clock cycles.
+constexpr int kStampWords = 6;
+
 constexpr int kAppendTokens = 16;  // tokens per append item of a fused append + attention launch
 constexpr int kAppendDoneOffset = 128;  // byte offset of the append completion counter in the workspace header
 // Status words at the start of the workspace (reset by every call's metadata upload):
@@ -110,7 +114,7 @@ struct AttnArgs {
   int32_t total_rows;
   int32_t n_items;
   int32_t n_tasks;
-  int64_t* stamps;   // NULL, or [n_items][4] {start, end, kind, request} in wall-clock ticks
+  int64_t* stamps;   // NULL, or [n_items][kStampWords] {start, end, kind, request, clk_start, clk_end}
   // fused append (n_append > 0): the first n_append items copy k_new / v_new
   // [sum(E), Hkv, D] into the cache; every wave of them adds 1 to *append_done
   // (release), and attention items that read new keys wait for n_append * kWaves

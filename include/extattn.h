@@ -323,12 +323,15 @@ int extattn_extend_attention_append(const void* q, const void* k_new, const void
  * token-budget blog, section 5) next to the chunk rows' span.
  *
  * Arguments as for extattn_extend_attention, plus:
- * stamps:   device int64 [capacity][4]; item i writes {start, end, kind,
- *           request}: start / end in ticks of the device's constant-rate wall
- *           clock, kind 0 for chunk rows and 1 for decode / verify rows, request
- *           the index into prefix_lens. Items are in launch order. The combine
- *           kernel that follows split items is not recorded.
- * capacity: number of 4-entry records stamps can hold; 0 (stamps NULL) asks
+ * stamps:   device int64 [capacity][6]; item i writes {start, end, kind,
+ *           request, clk_start, clk_end}: start / end in ticks of the device's
+ *           constant-rate wall clock, kind 0 for chunk rows and 1 for decode /
+ *           verify rows, request the index into prefix_lens, clk_start / clk_end
+ *           the shader-clock cycle counter of the workgroup's CU at the same two
+ *           points (so that cycles / ticks * tick_hz is the clock the kernel ran
+ *           at). Items are in launch order. The combine kernel that follows split
+ *           items is not recorded.
+ * capacity: number of 6-entry records stamps can hold; 0 (stamps NULL) asks
  *           only for n_items and returns EXTATTN_ENOSPC without enqueuing work.
  * n_items:  host out: the launch's number of work items.
  * tick_hz:  host out: wall-clock ticks per second of the current device.

@@ -88,6 +88,32 @@ def test_verify_rows_long_contexts():
     check_launch(sub, out, lse, q_off, q, what="verify rows, long contexts")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_verify_rows_40_to_64(d):
+    """Verify rows of 5..8 tokens with 64 query / 8 KV heads: 40, 48, 56 and 64 rows
+    per KV head, past the split path's 32, run as chunk tiles of few rows whose key
+    ranges are cut into split-length pieces and merged by the combine kernel.
+    Contexts from a few keys to two 8192-key pieces; every row of every request is
+    compared, and the measurement variant gives the same bits."""
+    launches = [(3, 5), (1000, 6), (4090, 7), (9000, 8), (250, 8), (16000, 5)]
+    w = custom_workload(71 + d, launches, 64, 8, d)
+    log(f"verify rows of 40..64 rows per KV head, D={d}")
+    out, lse, q_off, q = run_launch(w)
+    check_launch(w, out, lse, q_off, q, what=f"verify rows 40..64, D={d}")
+    cache = PagedCache(w)
+    for r in w.requests:
+        p, e = r.launch
+        cache.append([r.index], [0], w.k(r, 0, p + e), w.v(r, 0, p + e), [p + e])
+    qd = dev_tensor(q, w.dtype)
+    o2 = torch.empty_like(qd)
+    l2 = torch.empty_like(lse)
+    _, st, _ = ext.extend_attention(qd, cache.k, cache.v, cache.bt, [p for p, _ in launches],
+                                    [e for _, e in launches], w.scale, o2, l2, timed=True)
+    torch.cuda.synchronize()
+    assert set(st[:, 2].cpu().numpy().tolist()) == {0}, "rows of 40..64 are chunk tiles"
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
 def test_long_chunk_from_empty_prefix():
     """The largest chunk of the pages' workloads and then some: one 32768-token prompt
     from an empty cache (32 / 8 heads: 512 tiles per KV head, keys up to 32768),
@@ -165,8 +191,11 @@ def test_timed_variant_same_results_and_sane_stamps():
                              f"{float(d.nan_to_num(1e9).max())}, NaN {int(torch.isnan(out.float()).sum())}/"
                              f"{int(torch.isnan(o2.float()).sum())}; lse rows {lrows[:16]} ({len(lrows)})")
     st = st.cpu().numpy()
-    assert hz > 0 and st.shape[1] == 4 and st.shape[0] > 0
+    assert hz > 0 and st.shape[1] == 6 and st.shape[0] > 0
     assert (st[:, 1] >= st[:, 0]).all() and (st[:, 0] > 0).all()
+    # shader-clock cycles over wall-clock time: a clock between 0.5 and 3.5 GHz
+    sclk = (st[:, 5] - st[:, 4]).sum() / ((st[:, 1] - st[:, 0]).sum() / hz)
+    assert (st[:, 5] >= st[:, 4]).all() and 0.5e9 < sclk < 3.5e9, sclk
     assert set(st[:, 2].tolist()) == {0, 1}
     kinds = {int(r): int(k) for k, r in zip(st[:, 2], st[:, 3])}
     assert kinds == {0: 1, 1: 0, 2: 1, 3: 1}, kinds   # rows per KV head: 4, 2400, 20, 4
