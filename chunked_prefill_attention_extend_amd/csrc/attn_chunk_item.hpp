@@ -16,8 +16,9 @@
 //    every MFMA has a share of the exponentials beside it (two waves per SIMD then
 //    keep the matrix core and the vector ALU busy together).
 //  * K and V tiles go from the paged cache straight into 8-slot LDS rings
-//    (global_load_lds_dwordx4), 6 and 4 tiles ahead of their P.V step, with one
-//    barrier every two steps; each wave copies one 1 KB piece of every tile.
+//    (global_load_lds_dwordx4), 8 and 6 tiles ahead of their P.V step, with one
+//    barrier every two steps that leaves the last four steps' copies in flight; each
+//    wave copies one 1 KB piece of every tile.
 //  * Scores are the fp32 products of the given bf16 q and k; the weights are
 //    2^(s c - m), c = scale * log2(e), one fma and one exp2 per score, so lse is the
 //    log-sum-exp of exactly those scores. m is the first tile's exact row max; a wave
@@ -137,7 +138,16 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
   constexpr int NINST = PIECES >= WAVES ? PIECES / WAVES : 1;  // per wave and tile (waves past PIECES copy none)
   constexpr int THREADS = 64 * WAVES;
   constexpr int RING = kChunkRing;                // LDS ring slots per operand (= loop unroll)
-  constexpr int KLEAD = 6, VLEAD = 4;             // tiles a copy runs ahead of its step's P.V tile
+  constexpr int KLEAD = 8, VLEAD = 6;             // tiles a copy runs ahead of its step's P.V tile
+  // Copies issued in the last OUT steps may still be in flight at a barrier: the two
+  // steps after a barrier read K(u+3), K(u+4), V(u+1), V(u+2), issued KLEAD - 2 and
+  // VLEAD steps before their reads, so OUT <= min(KLEAD - 4, VLEAD - 2). A K copy
+  // overwrites the slot last read 2 steps earlier and a V copy the slot last read
+  // 8 - VLEAD steps earlier, each across a barrier (barriers follow odd steps), so
+  // KLEAD <= 8 and VLEAD <= 6 with 8 slots.
+  constexpr int OUT = (KLEAD - 4 < VLEAD - 2) ? KLEAD - 4 : VLEAD - 2;
+  static_assert(KLEAD <= RING && VLEAD <= RING - 2 && KLEAD >= VLEAD && OUT >= 1 && KLEAD % 2 == 0,
+                "ring leads");
   constexpr int KBUF = 0, VBUF = RING * KT_BYTES, IDBUF = 2 * RING * KT_BYTES;
   constexpr int PPS = 8 / KS;                     // weight pairs of a row block per interleave slot
   static_assert(KS == NB, "one Q.K and one P.V product per row block and slot");
@@ -188,6 +198,12 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
   // LDS operand reads (swizzles as in the helpers' layout description).
   const int k_off0 = key_of_row(l32) * (D * 2) + (((hi ^ (l32 & 15)) & (NC - 1)) << 4);
   const int v_off = l32 * (kBlockSize * 2) + ((hi ^ swz_v(l32)) << 4);
+  // This lane's V-ring base, held in a register: the ring sits above 64 KB, so with
+  // the ring's offset folded into each read's address the reads would each need an
+  // add; from this base every slot and sub-tile offset fits the reads' 16-bit
+  // immediate.
+  uint32_t vbase = lds_addr(smem + VBUF) + uint32_t(v_off);
+  asm volatile("" : "+v"(vbase));
 
   const int t0 = it.key_begin / KT;
   const int t1 = (it.key_end + KT - 1) / KT;
@@ -197,10 +213,10 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
   // loads (wave 0); window k covers tiles t0 + 32k .. t0 + 32k + 31 and sits in ring
   // half k & 1. From there each lane holds the 64-bit K and V source addresses of one
   // (tile, 16-key block) entry, lane (tile & 31) * 2 + block, so that a copy needs two
-  // readlanes and no scalar arithmetic. Step u copies K of tile u + 6 and V of tile
-  // u + 4, so the register is refreshed half at a time: the lower half (tiles 32k ..
-  // 32k+15) at step 32k - 6, the upper half at step 32k + 10, each after the last
-  // copy that read the entries it replaces. Entries past the sequence end or past the range,
+  // readlanes and no scalar arithmetic. Step u copies K of tile u + KLEAD and V of
+  // tile u + VLEAD, so the register is refreshed half at a time: the lower half (tiles
+  // 32k .. 32k+15) at step 32k - KLEAD, the upper half at step 32k + 16 - KLEAD, each
+  // after the last copy that read the entries it replaces. Entries past the sequence end or past the range,
   // and ids outside [0, num_blocks), point at the zero page; the invalid ones are
   // reported as their entries are made.
   int32_t* id_ring = reinterpret_cast<int32_t*>(smem + IDBUF);
@@ -385,9 +401,12 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
       clip_tail((n - 1) % RING);
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    // otherwise its V lands by the barrier after step bclip (odd, within 4 steps of
-    // the copy) and is cleared there, before step n-1 reads it
-    const int bclip = ((n - 4) & 1) ? n - 4 : n - 3;
+    // otherwise its V (copied at step n-1-VLEAD) has landed by the barrier after
+    // step bclip (odd, bclip - OUT >= n-1-VLEAD) and is cleared there, before step
+    // n-1 reads it
+    const int bfirst = n - 1 - VLEAD + OUT;
+    const int bclip = (bfirst & 1) ? bfirst : bfirst + 1;
+    static_assert(OUT <= VLEAD - 2, "bclip <= n - 2: the clip lands before step n-1");
     f32x16 sa[RB], sb[RB];
     u32x4 pa[RB][2], pb[RB][2];
     float la[RB], lb[RB];
@@ -406,6 +425,9 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
       }
       qk(std::integral_constant<int, 1>{}, sb);
     }
+    // Steps 0 and 1 copy K of tiles KLEAD and KLEAD+1 into the slots of tiles
+    // KLEAD-8 and KLEAD-7; with KLEAD = 8 those are tiles 0 and 1, read just above.
+    if constexpr (KLEAD > RING - 2) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // Step u (tile j = t0 + u): on entry tile j's weights are in px / lsx and S(j+1)
     // (raw) is in sy; K(j+2) sits in K slot (u+2)%RING and V(j) in V slot u%RING. The step
@@ -414,23 +436,24 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
     //     and the P.V products of tile j for both blocks, next to the exps of tile
     //     j+1's weights (masked if diagonal; packed and summed one slot later, into
     //     py / lsy),
-    //   issues the copies of K(j+6) (slot last read in step u-4) and V(j+4) (slot
-    //     last read in step u-4) half way,
-    //   and, after odd steps only, waits for the copies issued before this step and
+    //   issues the copies of K(j+KLEAD) (slot last read in step u-2) and V(j+VLEAD)
+    //     (slot last read in step u+VLEAD-8) half way,
+    //   and, after odd steps only, waits for the copies issued up to step u-OUT and
     //     meets the other waves. Between a slot's last read and its next copy, and
-    //     between a copy and its first read, lie at least one such barrier (the copy
-    //     issued at least one step before it).
+    //     between a copy and its first read, lie at least one such barrier (see OUT).
     auto step = [&](auto slot_tag, auto mask_tag, int u, f32x16 (&sx)[RB], f32x16 (&sy)[RB], u32x4 (&px)[RB][2],
                     u32x4 (&py)[RB][2], float (&lsx)[RB], float (&lsy)[RB]) {
       constexpr int sl = decltype(slot_tag)::value;  // u % RING
       constexpr bool diag = decltype(mask_tag)::value;  // tile j+1 may need the causal mask
       const int j = t0 + u;
-      // entries: the lower half of window (u + 6) / 32 at u = 26 (mod 32), its upper
-      // half at u = 10 (mod 32) (from step 42 on; window 0 came whole); the next
+      // entries: the lower half of window (u + KLEAD) / 32 at u = 32 - KLEAD (mod 32),
+      // its upper half at u = 16 - KLEAD (mod 32) (from step 48 - KLEAD on; window 0
+      // came whole), each after the last copy (of V, VLEAD behind K) that used the
+      // entries it replaces; the next
       // window's ids replace the ring half of the window before at u = 0 (mod 32)
       if constexpr (sl % 2 == 0) {
-        if ((u & 31) == 26) make_entries((u + KLEAD) >> 5, 0);
-        if ((u & 31) == 10 && u >= 42) make_entries((u + KLEAD) >> 5, 1);
+        if ((u & 31) == 32 - KLEAD) make_entries((u + KLEAD) >> 5, 0);
+        if ((u & 31) == 16 - KLEAD && u >= 48 - KLEAD) make_entries((u + KLEAD) >> 5, 1);
         if ((u & 31) == 0 && u > 0) fill_ids((u >> 5) + 1);
       }
       auto issue = [&]() {
@@ -450,10 +473,12 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
         __builtin_amdgcn_sched_barrier(0);
         constexpr int slk = (sl + 2) % RING;  // K slot of tile j+2
         const unsigned char* kb = smem + KBUF + slk * KT_BYTES;
-        const unsigned char* vb = smem + VBUF + sl * KT_BYTES + v_off;
+        typedef __attribute__((address_space(3))) const unsigned char lds_byte;
+        typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+        lds_byte* vb = reinterpret_cast<lds_byte*>(vbase) + sl * KT_BYTES;
         auto kread = [&](int t) -> u32x4 { return *reinterpret_cast<const u32x4*>(kb + (k_off0 ^ (t << 5))); };
         auto vread = [&](int i) -> u32x4 {
-          return *reinterpret_cast<const u32x4*>(vb + (i / DB) * VSUB + (i % DB) * 32 * (kBlockSize * 2));
+          return *reinterpret_cast<lds_u32x4*>(vb + (i / DB) * VSUB + (i % DB) * 32 * (kBlockSize * 2));
         };
         u32x4 kf[KS], vf[NB];
         float e[RB][16];
@@ -515,7 +540,7 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
         }
       }
       if constexpr (sl % 2 == 1) {
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(kIssuePerStep) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(OUT * kIssuePerStep) : "memory");
         if (tail_clip && n > VLEAD && u == bclip) {  // V of the last tile has landed
           clip_tail((n - 1) % RING);
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
