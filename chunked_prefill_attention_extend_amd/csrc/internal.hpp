@@ -21,7 +21,7 @@ constexpr int kSplitKeysMin = 1024;  // split path: keys per workgroup (kWaves w
 constexpr int kSplitKeysMax = 8192;  // upper bound: a wave's block ids fit one per lane
 constexpr int kSplitTargetItems = 256;  // split path aims at this many workgroups (1 per CU on 256 CUs)
 constexpr int kChunkTargetItems = 256;  // chunk rows: split key ranges until about this many workgroups (1 per CU)
-constexpr int kChunkMinPieceKeys = 2048;  // ... with at least this many keys per piece
+constexpr int kChunkMinPieceKeys = 1024;  // ... with at least this many keys per piece
 constexpr int kCombineRows = 32;         // rows per combine task of split chunk tiles
 constexpr int kXcds = 8;  // accelerator dies (own L2 each); a launch's workgroups are dealt to them round-robin
 constexpr int kSplitRows = 16;    // split path: rows of one 16-row MFMA block

@@ -69,3 +69,46 @@ def test_noalloc_refuses_launches_beyond_the_scratch():
     out = torch.empty_like(q)
     with pytest.raises(ValueError, match="workspace too small"):
         ext.extend_attention_noalloc(q, k_cache, v_cache, bt, [ctx - 1] * n, [1] * n, 1.0 / np.sqrt(d), out)
+
+
+def test_noalloc_under_graph_capture():
+    """The allocation-free call captured in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed: its metadata travels in the captured kernels' arguments and the scratch
+    is static, so every replay, with eager work and a synchronization between
+    replays, gives the eager call's bits and clean status words."""
+    launches, hq, hkv, d, seed = [(3000, 1), (2000, 300), (40, 1)], 32, 8, 128, 33
+    w = custom_workload(seed, launches, hq, hkv, d)
+    cache = PagedCache(w)
+    for r in w.requests:
+        p, e = r.launch
+        cache.append([r.index], [0], w.k(r, 0, p + e), w.v(r, 0, p + e), [p + e])
+    q = dev_tensor(np.concatenate([w.q(r, r.launch[0], r.launch[0] + r.launch[1]) for r in w.requests]), w.dtype)
+    prefix = [r.launch[0] for r in w.requests]
+    extend = [r.launch[1] for r in w.requests]
+    o_ref = torch.empty_like(q)
+    l_ref = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    log("graph capture: eager reference call")
+    ext.extend_attention_noalloc(q, cache.k, cache.v, cache.bt, prefix, extend, w.scale, o_ref, l_ref, check=True)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full_like(l_ref, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the side stream before capture
+        ext.extend_attention_noalloc(q, cache.k, cache.v, cache.bt, prefix, extend, w.scale, out, lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    log("graph capture: capturing")
+    with torch.cuda.graph(g):
+        ext.extend_attention_noalloc(q, cache.k, cache.v, cache.bt, prefix, extend, w.scale, out, lse)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))  # eager work between the replays
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        log(f"graph capture: replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        flags, bad, _ = ext.read_status(None)
+        assert flags == 0 and bad == 0, f"replay {rep}: status {flags:#x} / {bad}"
+        assert torch.equal(out, o_ref) and torch.equal(lse, l_ref), f"replay {rep} differs from the eager call"
