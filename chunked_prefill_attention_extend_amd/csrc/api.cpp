@@ -462,7 +462,7 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
     if (e != hipSuccess) return hip_fail(e, "fp32 attention launch");
   } else {
     if (a.n_items > 0) {
-      // launches of chunk rows only (and their fused appends) run on the 4-wave chunk
+      // launches of chunk rows only (and their fused appends) run on the 8-wave chunk
       // kernel; decode / verify rows need the mixed kernel, which takes every item
       e = plan.n_split > 0 ? launch_attn_bf16(a, st) : launch_chunk_bf16(a, st);
       if (e != hipSuccess) return hip_fail(e, "bf16 attention launch");

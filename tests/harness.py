@@ -20,7 +20,7 @@ from synth import Workload
 
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
-# Tolerances. out: the benchmark spec's bars for bf16 inputs with fp32 accumulation
+# Tolerances. out: the required bars for bf16 inputs with fp32 accumulation
 # (max abs 2e-2, mean abs 2e-3) and for fp32 (1e-5). lse (natural log): 1e-3 for
 # bf16 inputs, 1e-5 for fp32, against the exact fp64 log-sum-exp of the scaled
 # scores. The kernels form every score from the unmodified inputs and sum the
