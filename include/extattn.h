@@ -24,8 +24,9 @@
  *    owns every buffer. Device work is enqueued on `stream` (a hipStream_t;
  *    NULL means the default stream) and the call returns without waiting;
  *    outputs are valid once the stream has reached that point. The library
- *    keeps a pool of pinned host staging buffers per device for the small
- *    metadata it copies to the workspace (a buffer is reused once the copy
+ *    keeps a pool of pinned host staging buffers per device (coherent and
+ *    mapped into the device) for the small metadata that a copy kernel on
+ *    `stream` moves into the workspace (a buffer is reused once the copy
  *    that last read it has completed; the pool grows instead of waiting, up to
  *    512 buffers in flight per device, beyond which a call waits on the host
  *    for the oldest copy to finish), and a bounded host table of launch plans
