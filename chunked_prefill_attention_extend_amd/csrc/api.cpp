@@ -463,8 +463,9 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
   } else {
     if (a.n_items > 0) {
       // launches of chunk rows only (and their fused appends) run on the 8-wave chunk
-      // kernel; decode / verify rows need the mixed kernel, which takes every item
-      e = plan.n_split > 0 ? launch_attn_bf16(a, st) : launch_chunk_bf16(a, st);
+      // kernel; decode / verify rows need the mixed kernel, which takes every item,
+      // or, when some request has 33-64 rows and none more, the 4-wave wide kernel
+      e = plan.wide ? launch_split_wide(a, st) : plan.n_split > 0 ? launch_attn_bf16(a, st) : launch_chunk_bf16(a, st);
       if (e != hipSuccess) return hip_fail(e, "bf16 attention launch");
     }
     if (a.n_tasks > 0) {

@@ -1,0 +1,306 @@
+// Split items of the bf16 path: decode rows and multi-token verify rows, each
+// wave streaming its own part of the key range from HBM into MFMA operand
+// registers (shared by the mixed kernel and the 4-wave wide-split kernel).
+#pragma once
+
+#include "attn_bf16_common.hpp"
+
+namespace extattn {
+
+// ---------------------------------------------------------------------------
+// Split items: <= 32 rows on the 8-wave kernels, <= 64 on the 4-wave wide-split
+// kernel (decode rows, multi-token verify rows); each of the W waves streams its
+// own part of the key range from HBM straight into MFMA operand registers. These
+// run on v_mfma_f32_16x16x32_bf16 with RB = 1 .. 4 blocks of 16 query rows per
+// wave; the RB blocks share every K/V operand, so the context is read once
+// whatever the row count. Accumulator element i of lane l belongs to
+// query row l % 16 of its block and MFMA row 4 (l / 16) + i; MFMA row r of key
+// block b holds key 8 (r / 4) + 4 b + r % 4 of the tile, so each lane's P^T
+// operand (4 values from block 0, 4 from block 1) covers 8 consecutive keys.
+// At 8 waves (256 registers a wave): with one row block two 32-key tiles are in
+// flight per wave; with two, the second block's operands take the registers of
+// the second tile, and the next tile is loaded as soon as the current one has
+// been consumed. At 4 waves (512 registers) a ring of 3-4 tiles.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+template <int D, int RB, int W>
+__device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char* smem) {
+  constexpr int KS = D / 32;  // 32-wide k-steps over the head dim
+  constexpr int DB = D / 16;  // 16-feature blocks of O^T
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const SeqInfo si = a.seqs[it.seq];
+  const int G = a.group, g = it.kv_head;
+  const int kv_len = si.prefix + si.extend;
+
+  // Row block rb of this lane: row rb * 16 + l16 of the item.
+  // At 3-4 row blocks on the wide kernel Q stays in LDS (an image of the operand
+  // registers after the merge area, written once by wave rb for block rb) and is
+  // read where each product uses it; the registers go to the K/V ring instead.
+  constexpr bool QLDS = W == kWideWaves && RB >= 3;
+  const uint32_t qimg = lds_addr(smem) + uint32_t(W * RB * kSplitRows * (D + 2) * 4);
+  u32x4 qf[RB][KS];
+  int lim[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rr = rb * kSplitRows + l16;
+    const bool valid = rr < it.nrows;
+    const int pos = valid ? rr / G : 0;
+    const int hh = valid ? rr - pos * G : 0;
+    const int64_t orow = int64_t(si.q_off + pos) * a.hq + g * G + hh;
+    lim[rb] = valid ? min(si.prefix + pos, it.key_end - 1) : -1;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + orow * D + q4 * 8;
+    if constexpr (QLDS) {
+      if (rb == wave) {
+        typedef __attribute__((address_space(3))) u32x4 lds_q_t;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          *reinterpret_cast<lds_q_t*>(qimg + uint32_t(((rb * KS + ks) * 64 + lane) * 16)) =
+              valid ? *reinterpret_cast<const u32x4*>(qp + ks * 32) : zero4();
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[rb][ks] = valid ? *reinterpret_cast<const u32x4*>(qp + ks * 32) : zero4();
+    }
+  }
+  if constexpr (QLDS) __syncthreads();
+  const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
+  const int nblk = (kv_len + kBlockSize - 1) / kBlockSize;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+
+  f32x4 o[RB][DB];
+  float m[RB], l[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+  }
+
+  // Keys (within the 32-key tile) this lane loads as MFMA rows of blocks 0 / 1.
+  const int kbase = 8 * (l16 >> 2) + (l16 & 3);
+  // This wave's tiles [tw0, tw1) of the item's key range.
+  const int nt = (it.key_end - it.key_begin + kSplitTile - 1) / kSplitTile;
+  const int tw0 = wave * nt / W, tw1 = (wave + 1) * nt / W;
+  // All block ids of the wave's range in one load (one per lane), checked once:
+  // ids outside [0, num_blocks) become -1 (read the zero page) and are counted;
+  // entries past the sequence end are -1 too. No tile load then waits on an id.
+  static_assert(split_keys_max(W) / kSplitTile / W * (kSplitTile / kBlockSize) <= 64, "ids of a wave fit one per lane");
+  int32_t idw = -1;
+  {
+    const int lb = (it.key_begin + tw0 * kSplitTile) / kBlockSize + lane;
+    const bool inside = lane < (tw1 - tw0) * (kSplitTile / kBlockSize) && lb < nblk;
+    const int32_t v = inside ? bt[lb] : -1;
+    const bool ok = block_ok(v, a.num_blocks);
+    const uint64_t bad = __builtin_amdgcn_ballot_w64(inside && !ok);
+    if (bad != 0 && lane == 0) report_bad_blocks(a.err, int(__builtin_popcountll(bad)));
+    idw = (inside && ok) ? v : -1;
+  }
+  const unsigned char* zp = static_cast<const unsigned char*>(a.zero_page);
+  auto blk_base = [&](const uint16_t* cache, int32_t blk) -> const uint16_t* {
+    return blk < 0 ? reinterpret_cast<const uint16_t*>(zp) : cache + (int64_t(blk) * a.hkv + g) * (kBlockSize * D);
+  };
+  struct Tile {
+    u32x4 kf[2][KS];
+    u32x4 vf[DB];
+    int kt;
+  };
+  // Loads are unconditional (invalid blocks and blocks past the end read the zero
+  // page); the sequence end is applied when the tile is consumed, so the next
+  // tile's loads stay in flight while this one is computed. Every K/V byte is read
+  // once here, so the loads carry the non-temporal hint (streamed, not kept in the
+  // caches): measured 5.35 TB/s for the decode rows against 4.1 TB/s without it.
+  auto load = [&](int jj, Tile& T) {
+    const int kt = it.key_begin + jj * kSplitTile;
+    // tiles loaded past the wave's range may index past lane 63: any valid id will do
+    const int e = (2 * (jj - tw0)) & 63;
+    const int32_t s0 = __builtin_amdgcn_readlane(idw, e), s1 = __builtin_amdgcn_readlane(idw, e + 1);
+    const uint16_t* kb0 = blk_base(kc, s0);
+    const uint16_t* kb1 = blk_base(kc, s1);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int koff = kbase + 4 * b;  // < 32; block koff / 16
+      const uint16_t* kp = (koff < kBlockSize ? kb0 : kb1) + (koff % kBlockSize) * D + q4 * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) T.kf[b][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + ks * 32));
+    }
+    const uint16_t* vp = (q4 < 2 ? blk_base(vc, s0) : blk_base(vc, s1)) + 8 * (q4 & 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) T.vf[db] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (db * 16 + l16) * kBlockSize));
+    T.kt = kt;
+  };
+  auto compute = [&](Tile& T) {
+    const int kt = T.kt;
+    u32x4 pf[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x4 sc[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if constexpr (QLDS) {
+            // an opaque address per tile: the compiler must not hoist these reads
+            // out of the loop into registers
+            uint32_t qa = qimg + uint32_t(((rb * KS + ks) * 64 + lane) * 16);
+            asm volatile("" : "+v"(qa));
+            typedef __attribute__((address_space(3))) const u32x4 lds_cq_t;
+            sc[b] = mfma16(T.kf[b][ks], *reinterpret_cast<lds_cq_t*>(qa), sc[b]);
+          } else {
+            sc[b] = mfma16(T.kf[b][ks], qf[rb][ks], sc[b]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kt + 8 * q4 + 4 * b + i > lim[rb]) sc[b][i] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[b][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[rb], mx * a.scale_log2);
+      if (mnew > m[rb]) {
+        const float alpha = __builtin_amdgcn_exp2f(m[rb] - mnew);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
+        l[rb] *= alpha;
+        m[rb] = mnew;
+      }
+      const float msafe = (m[rb] == -INFINITY) ? 0.f : m[rb];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[b][0], a.scale_log2, -msafe));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[b][1], a.scale_log2, -msafe));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[b][2], a.scale_log2, -msafe));
+        const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[b][3], a.scale_log2, -msafe));
+        l[rb] += (p0 + p1) + (p2 + p3);
+        pf[rb][2 * b] = pack2(p0, p1);
+        pf[rb][2 * b + 1] = pack2(p2, p3);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const u32x4 vv = clip_keys(T.vf[db], kt + 8 * q4, kv_len);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma16(vv, pf[rb], o[rb][db]);
+    }
+  };
+
+  if constexpr (W == kWideWaves) {
+    // One wave per SIMD with 512 registers: NT tiles in a ring, NT - 1 of them in
+    // flight while one is computed (loads unconditional, as below): 4 tiles at up
+    // to 2 row blocks, 2 at 3-4 (a third measured slower at 3 blocks, and spills at 4).
+    constexpr int NT = RB <= 2 ? 4 : 2;
+    Tile tl[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) load(tw0 + k, tl[k]);
+    for (int jj = tw0; jj < tw1; jj += NT) {
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        if (k == 0 || jj + k < tw1) compute(tl[k]);
+        load(jj + k + NT, tl[k]);
+      }
+    }
+  } else if constexpr (RB == 1) {
+    // Two tiles in flight. Loads are issued whether or not the tile is used (tiles
+    // past the wave's range read the zero page): a load under a branch would make
+    // the compiler wait for it where the branches join.
+    Tile ta, tb;
+    load(tw0, ta);
+    for (int jj = tw0; jj < tw1; jj += 2) {
+      load(jj + 1, tb);
+      compute(ta);
+      load(jj + 2, ta);
+      if (jj + 1 < tw1) compute(tb);
+    }
+  } else {
+    Tile ta;
+    load(tw0, ta);
+    for (int jj = tw0; jj < tw1; ++jj) {
+      compute(ta);
+      load(jj + 1, ta);
+    }
+  }
+
+  // Merge the waves' partial results through LDS (the page's merge rule over the
+  // W parts): part[w][row][d] holds unnormalised o, mls[w][row] = (m, l).
+  constexpr int SR = RB * kSplitRows;  // rows per wave and rows of the partial slot
+  float* part = reinterpret_cast<float*>(smem);
+  float* mls = part + W * SR * D;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float lt = l[rb] + __shfl_xor(l[rb], 16);
+    lt += __shfl_xor(lt, 32);
+    const int rr = rb * kSplitRows + l16;
+    if (rr < it.nrows) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<float4*>(part + (wave * SR + rr) * D + db * 16 + 4 * q4) =
+            float4{o[rb][db][0], o[rb][db][1], o[rb][db][2], o[rb][db][3]};
+      if (q4 == 0) {
+        mls[(wave * SR + rr) * 2] = m[rb];
+        mls[(wave * SR + rr) * 2 + 1] = lt;
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int TPR = D / 4;           // threads per row, 4 features each
+  constexpr int RPP = 64 * W / TPR;  // rows per pass
+  const int c4 = (tid % TPR) * 4;
+#pragma unroll
+  for (int r0 = 0; r0 < SR; r0 += RPP) {
+    const int r = r0 + tid / TPR;
+    if (r >= it.nrows) continue;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f, M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, mls[(w * SR + r) * 2]);
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float lw = mls[(w * SR + r) * 2 + 1];
+        if (lw > 0.f) {
+          const float f = __builtin_amdgcn_exp2f(mls[(w * SR + r) * 2] - M);
+          const float4 ow = *reinterpret_cast<const float4*>(part + (w * SR + r) * D + c4);
+          L += f * lw;
+          acc.x += f * ow.x;
+          acc.y += f * ow.y;
+          acc.z += f * ow.z;
+          acc.w += f * ow.w;
+        }
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float lse_wg = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+    const float4 res = float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    if (it.task < 0) {  // this workgroup covered the whole key range
+      const int rpos = r / G;
+      const int64_t orow_r = int64_t(si.q_off + rpos) * a.hq + g * G + (r - rpos * G);
+      uint16_t* op = static_cast<uint16_t*>(a.out) + orow_r * D + c4;
+      u32x2 pk = {pack2(res.x, res.y), pack2(res.z, res.w)};
+      *reinterpret_cast<u32x2*>(op) = pk;
+      if (c4 == 0 && a.lse) a.lse[orow_r] = lse_wg;
+    } else {
+      // Leave this workgroup's partial (normalised o, natural-log lse) in its slot;
+      // the combine kernel merges the workgroups' partials of the task.
+      float* sl = a.slots + it.slot;  // rows [SR][D], then lse [SR]
+      *reinterpret_cast<float4*>(sl + r * D + c4) = res;
+      if (c4 == 0) sl[SR * D + r] = lse_wg;
+    }
+  }
+}
+
+}  // namespace extattn

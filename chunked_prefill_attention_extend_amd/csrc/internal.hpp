@@ -26,6 +26,11 @@ constexpr int kCombineRows = 32;         // rows per combine task of split chunk
 constexpr int kXcds = 8;  // accelerator dies (own L2 each); a launch's workgroups are dealt to them round-robin
 constexpr int kSplitRows = 16;    // split path: rows of one 16-row MFMA block
 constexpr int kSplitMaxRows = 32; // split path: at most this many rows (two blocks per wave)
+constexpr int kWideWaves = 4;      // wide-split kernel: wave64 per workgroup, one per SIMD, 512 registers each
+constexpr int kWideMaxRows = 64;   // ... at most this many rows per split item (four 16-row blocks per wave)
+constexpr int kWideKeysMax = 4096; // ... keys per workgroup: a wave's block ids fit one per lane
+// keys per split workgroup of `waves` waves, upper bound
+constexpr int split_keys_max(int waves) { return waves == kWideWaves ? kWideKeysMax : kSplitKeysMax; }
 constexpr int kFewRows = 2 * kRowsPerWave;  // chunk tiles of at most this many rows are cut into split-length key pieces
 
 // Per-request metadata copied to the workspace.
@@ -38,7 +43,7 @@ struct SeqInfo {
 
 enum : int32_t {
   kItemChunk = 0,  // kRowsPerTile rows of one (request, KV head); all waves share LDS K/V tiles
-  kItemSplit = 1,  // <= kSplitMaxRows rows; each wave takes its own part of the key range
+  kItemSplit = 1,  // <= kSplitMaxRows rows (kWideMaxRows in wide launches); each wave takes its own part of the key range
   kItemAppend = 2, // fused append: copy new tokens [row0, row0 + nrows) of a request into the cache
 };
 
@@ -61,7 +66,7 @@ struct WorkItem {
   int32_t seq;
   int32_t kv_head;
   int32_t row0;       // first flattened row
-  int32_t nrows;      // rows in this item (<= kRowsPerTile chunk, <= kSplitMaxRows split)
+  int32_t nrows;      // rows in this item (<= kRowsPerTile chunk, <= kSplitMaxRows or kWideMaxRows split)
   int32_t key_begin;  // keys [key_begin, key_end); key_begin is a multiple of kChunkKeys
   int32_t key_end;
   int32_t slot;       // < 0: write out/lse directly; else float offset of this item's partial slot
@@ -151,6 +156,7 @@ struct Plan {
   int32_t split_keys = 0;  // keys per split workgroup (0: no split items)
   int32_t n_append = 0;    // append items at the head of `items` (fused append launch)
   int32_t n_split = 0;     // split items (decode / verify rows) in `items`
+  bool wide = false;       // every split item runs on the 4-wave wide-split kernel (up to kWideMaxRows rows)
   int64_t total_rows = 0;
   // byte offsets inside the workspace
   size_t off_zero = 0, off_seqs = 0, off_items = 0, off_tasks = 0, off_slots = 0, bytes = 0, upload_bytes = 0;
@@ -216,6 +222,7 @@ int decode_first_with_slack_impl(int64_t ready_decode, int64_t pending_prefill, 
 // kernel launchers (one per .hip file)
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bf16(const AttnArgs& a, hipStream_t stream);  // chunk and append items only
+hipError_t launch_split_wide(const AttnArgs& a, hipStream_t stream);  // split and append items only
 hipError_t launch_combine(const AttnArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const KvArgs& a, int32_t dtype, hipStream_t stream);

@@ -209,13 +209,22 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
     // loads in flight) while it holds its CU alone, so pieces are as long as the
     // work allows while still giving about kSplitTargetItems workgroups; a multiple
     // of kWaves tiles, between kSplitKeysMin and kSplitKeysMax.
-    int64_t split_keys = 0;
-    for (int32_t r = 0; r < num_seqs; ++r)
+    int64_t split_keys = 0, max_rows = 0;
+    for (int32_t r = 0; r < num_seqs; ++r) {
       if (int64_t(extend[r]) * group <= kFewRows) split_keys += (int64_t(prefix[r]) + extend[r]) * hkv;
-    constexpr int64_t kGrain = int64_t(kSplitTile) * kWaves;
+      max_rows = std::max<int64_t>(max_rows, int64_t(extend[r]) * group);
+    }
+    // Launches of decode / verify rows only, some past the 8-wave split items'
+    // kSplitMaxRows rows (and none past kWideMaxRows): every request becomes split
+    // items of the 4-wave wide kernel, which reads each context once for up to 64
+    // rows.
+    plan.wide = max_rows > kSplitMaxRows && max_rows <= kWideMaxRows;
+    const int64_t split_max_rows = plan.wide ? kWideMaxRows : kSplitMaxRows;
+    const int split_waves = plan.wide ? kWideWaves : kWaves;
+    const int64_t kGrain = int64_t(kSplitTile) * split_waves;
     int64_t piece = (split_keys + kSplitTargetItems - 1) / kSplitTargetItems;
     piece = (piece + kGrain - 1) / kGrain * kGrain;
-    piece = std::min<int64_t>(std::max<int64_t>(piece, kSplitKeysMin), kSplitKeysMax);
+    piece = std::min<int64_t>(std::max<int64_t>(piece, kSplitKeysMin), split_keys_max(split_waves));
     plan.split_keys = int32_t(piece);
     // Chunk rows: when the chunk tiles alone cannot fill the GPU (short chunks, few
     // heads), each tile's key range is cut into pieces, one workgroup each, and the
@@ -224,15 +233,15 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
     int64_t chunk_tiles = 0;
     for (int32_t r = 0; r < num_seqs; ++r) {
       const int64_t rows = int64_t(extend[r]) * group;
-      if (rows > kSplitMaxRows) chunk_tiles += (rows + kRowsPerTile - 1) / kRowsPerTile * hkv;
+      if (rows > split_max_rows) chunk_tiles += (rows + kRowsPerTile - 1) / kRowsPerTile * hkv;
     }
     const int64_t chunk_pieces =
         chunk_tiles > 0 ? std::max<int64_t>(1, (kChunkTargetItems + chunk_tiles - 1) / chunk_tiles) : 1;
     for (int32_t r = 0; r < num_seqs; ++r) {
       const int64_t rows = int64_t(extend[r]) * group;
       const int64_t kv_len = int64_t(prefix[r]) + extend[r];
-      if (rows <= kSplitMaxRows) {
-        const int32_t srows = rows <= kSplitRows ? kSplitRows : kSplitMaxRows;  // rows of a partial slot
+      if (rows <= split_max_rows) {
+        const int32_t srows = int32_t((rows + kSplitRows - 1) / kSplitRows * kSplitRows);  // rows of a partial slot
         const int64_t nwg = (kv_len + piece - 1) / piece;
         const int64_t sf = int64_t(slot_floats(srows, head_dim));
         for (int32_t g = 0; g < hkv; ++g) {

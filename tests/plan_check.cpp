@@ -3,12 +3,14 @@
 //
 // For every random launch (request mix of chunk, verify and decode rows; GQA group;
 // head dim; with and without the fused append) the work list must:
+//  * run decode / verify-only launches with 33-64 rows on the wide-split kernel;
 //  * cover every (request, KV head, row, key) pair a row attends exactly once, with
 //    key ranges that start on 32-key tile boundaries and never pass the row's last
 //    visible key's tile;
 //  * give every item of a split key range its own partial slot, inside the slot area,
 //    and give the slots' rows to combine tasks that cover each row of the range once;
-//  * keep split items within the per-wave id budget (kSplitKeysMax keys);
+//  * keep split items within the per-wave id budget (kSplitKeysMax keys; kWideKeysMax
+//    on the 4-wave wide-split kernel) and the row limit of the kernel that runs them;
 //  * put the fused append's items first, covering each request's new tokens once;
 //  * keep the tiles of one chunk group (request, KV head) on a contiguous run of die
 //    lanes (list positions modulo kXcds) while every lane still has items.
@@ -46,6 +48,10 @@ static bool check_launch(const std::vector<int32_t>& P, const std::vector<int32_
   CHECK(rc == EXTATTN_OK, "seed %u: build_plan returned %d", seed, rc);
   const int G = hq / hkv;
   const int n = int(P.size());
+  // wide-split launches: decode / verify rows only, some past kSplitMaxRows, none past kWideMaxRows
+  int max_rows = 0;
+  for (int r = 0; r < int(E.size()); ++r) max_rows = std::max(max_rows, E[r] * G);
+  CHECK(plan.wide == (max_rows > kSplitMaxRows && max_rows <= kWideMaxRows), "seed %u: wide flag", seed);
   // 1. appends first, covering each request's new tokens once
   size_t first = 0;
   if (append) {
@@ -79,14 +85,17 @@ static bool check_launch(const std::vector<int32_t>& P, const std::vector<int32_
     const int kv_len = P[x.seq] + E[x.seq];
     CHECK(x.key_end <= kv_len, "seed %u: item %zu key_end %d > %d", seed, i, x.key_end, kv_len);
     if (x.kind == kItemSplit) {
-      CHECK(x.nrows <= kSplitMaxRows && rows <= kSplitMaxRows && x.row0 == 0, "seed %u: split item %zu rows", seed, i);
-      CHECK(x.key_end - x.key_begin <= kSplitKeysMax, "seed %u: split piece of %d keys", seed, x.key_end - x.key_begin);
+      const int smax = plan.wide ? kWideMaxRows : kSplitMaxRows;
+      CHECK(x.nrows <= smax && rows <= smax && x.row0 == 0, "seed %u: split item %zu rows", seed, i);
+      CHECK(x.key_end - x.key_begin <= split_keys_max(plan.wide ? kWideWaves : kWaves),
+            "seed %u: split piece of %d keys", seed, x.key_end - x.key_begin);
     } else {
+      CHECK(!plan.wide, "seed %u: chunk item %zu in a wide-split launch", seed, i);
       CHECK(x.nrows <= kRowsPerTile && x.row0 % kRowsPerTile == 0, "seed %u: chunk item %zu tile", seed, i);
     }
     if (x.slot >= 0) {
       CHECK(x.task >= 0 && size_t(x.task) < plan.tasks.size(), "seed %u: item %zu task", seed, i);
-      const int srows = x.kind == kItemChunk ? (x.nrows + 15) / 16 * 16 : (rows <= kSplitRows ? kSplitRows : kSplitMaxRows);
+      const int srows = x.kind == kItemChunk ? (x.nrows + 15) / 16 * 16 : (rows + 15) / 16 * 16;
       CHECK(x.slot_rows == srows, "seed %u: item %zu slot of %d rows, expected %d", seed, i, x.slot_rows, srows);
       CHECK(x.slot % 4 == 0, "seed %u: item %zu slot not 16-byte aligned", seed, i);
       slots.push_back({x.slot, x.slot + int64_t(slot_floats(srows, d))});
@@ -174,6 +183,22 @@ int main(int argc, char** argv) {
       E.push_back(kind == 3 ? 1 + int(g() % 700) : e);
     }
     if (!check_launch(P, E, h[0], h[1], d, (g() & 3) == 0, seed)) break;
+    ++done;
+  }
+  // launches of decode and verify rows only (wide-split launches among them)
+  for (int it = 0; it < launches / 2; ++it) {
+    const unsigned seed = rng();
+    std::mt19937 g(seed);
+    const auto& h = heads[g() % 6];
+    const int d = (g() & 1) ? 128 : 64;
+    const int nreq = 1 + int(g() % 40);
+    const int emax = 1 + int(g() % 8);
+    std::vector<int32_t> P, E;
+    for (int r = 0; r < nreq; ++r) {
+      P.push_back(int(g() % 30000));
+      E.push_back(1 + int(g() % emax));
+    }
+    if (fails || !check_launch(P, E, h[0], h[1], d, (g() & 3) == 0, seed)) break;
     ++done;
   }
   // the pages' workloads

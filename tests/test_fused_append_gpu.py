@@ -61,6 +61,7 @@ def _run_both(w):
     ([(5000, 1024)], 64, 8, 128, "bf16"),   # one sweep-like chunk, prefix ending inside a block
     ([(6000, 700)], 32, 8, 128, "bf16"),    # chunk tiles cut into key pieces (pure-prefix pieces do not wait)
     ([(777, 40), (33, 1), (0, 17)], 16, 2, 64, "bf16"),  # D=64
+    ([(3000, 5), (4000, 8), (12, 1), (9000, 7)], 64, 8, 128, "bf16"),  # 40-64 verify rows: wide kernel
     ([(50, 30), (129, 1)], 8, 2, 128, "f32"),  # fp32: append launch, then attention
 ])
 def test_fused_append_matches_separate(case):

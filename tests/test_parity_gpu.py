@@ -70,9 +70,10 @@ def test_edge_cases(case):
 
 
 def test_verify_rows_long_contexts():
-    """Verify rows of 1..16 tokens (4..64 rows per KV head: split items of one and
-    two row blocks, partial chunk tiles) over contexts long enough that the split
-    pieces reach their longest (8192 keys); ten requests compared."""
+    """Verify rows of 1..16 tokens (4..64 rows per KV head, so the launch runs on the
+    4-wave wide kernel: split items of one to four row blocks) over contexts long
+    enough that the split pieces reach their longest (4096 keys there); ten
+    requests compared."""
     rng = np.random.default_rng(41)
     n = 40
     ctx = rng.integers(4000, 9000, size=n, endpoint=True)
@@ -91,11 +92,13 @@ def test_verify_rows_long_contexts():
 @pytest.mark.parametrize("d", [128, 64])
 def test_verify_rows_40_to_64(d):
     """Verify rows of 5..8 tokens with 64 query / 8 KV heads: 40, 48, 56 and 64 rows
-    per KV head, past the split path's 32, run as chunk tiles of few rows whose key
-    ranges are cut into split-length pieces and merged by the combine kernel.
-    Contexts from a few keys to two 8192-key pieces; every row of every request is
-    compared, and the measurement variant gives the same bits."""
-    launches = [(3, 5), (1000, 6), (4090, 7), (9000, 8), (250, 8), (16000, 5)]
+    per KV head, past the 8-wave split items' 32, next to a decode row (8 rows) and
+    a 3-token row (24): the launch runs every request as split items of the 4-wave
+    wide kernel (one to four 16-row blocks per wave), key ranges cut into
+    4096-key pieces merged by the combine kernel. Contexts from a few keys to
+    several pieces; every row of every request is compared, and the measurement
+    variant gives the same bits."""
+    launches = [(3, 5), (1000, 6), (4090, 7), (9000, 8), (250, 8), (16000, 5), (7000, 1), (5000, 3)]
     w = custom_workload(71 + d, launches, 64, 8, d)
     log(f"verify rows of 40..64 rows per KV head, D={d}")
     out, lse, q_off, q = run_launch(w)
@@ -110,7 +113,7 @@ def test_verify_rows_40_to_64(d):
     _, st, _ = ext.extend_attention(qd, cache.k, cache.v, cache.bt, [p for p, _ in launches],
                                     [e for _, e in launches], w.scale, o2, l2, timed=True)
     torch.cuda.synchronize()
-    assert set(st[:, 2].cpu().numpy().tolist()) == {0}, "rows of 40..64 are chunk tiles"
+    assert set(st[:, 2].cpu().numpy().tolist()) == {1}, "rows of 40..64 run as split items"
     assert torch.equal(out, o2) and torch.equal(lse, l2)
 
 
