@@ -91,20 +91,29 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   // This wave's tiles [tw0, tw1) of the item's key range.
   const int nt = (it.key_end - it.key_begin + kSplitTile - 1) / kSplitTile;
   const int tw0 = wave * nt / W, tw1 = (wave + 1) * nt / W;
-  // All block ids of the wave's range in one load (one per lane), checked once:
-  // ids outside [0, num_blocks) become -1 (read the zero page) and are counted;
-  // entries past the sequence end are -1 too. No tile load then waits on an id.
-  static_assert(split_keys_max(W) / kSplitTile / W * (kSplitTile / kBlockSize) <= 64, "ids of a wave fit one per lane");
-  int32_t idw = -1;
-  {
-    const int lb = (it.key_begin + tw0 * kSplitTile) / kBlockSize + lane;
-    const bool inside = lane < (tw1 - tw0) * (kSplitTile / kBlockSize) && lb < nblk;
+  // All block ids of the wave's range in one or two loads (one per lane each),
+  // checked once: ids outside [0, num_blocks) become -1 (read the zero page) and
+  // are counted; entries past the sequence end are -1 too. No tile load then
+  // waits on an id.
+  constexpr int IDS = split_keys_max(W) / kSplitTile / W * (kSplitTile / kBlockSize);  // ids of a wave, at most
+  constexpr int IDR = (IDS + 63) / 64;
+  static_assert(IDR <= 2, "ids of a wave fit two per lane");
+  int32_t idw[IDR];
+#pragma unroll
+  for (int h = 0; h < IDR; ++h) {
+    const int lb = (it.key_begin + tw0 * kSplitTile) / kBlockSize + h * 64 + lane;
+    const bool inside = h * 64 + lane < (tw1 - tw0) * (kSplitTile / kBlockSize) && lb < nblk;
     const int32_t v = inside ? bt[lb] : -1;
     const bool ok = block_ok(v, a.num_blocks);
     const uint64_t bad = __builtin_amdgcn_ballot_w64(inside && !ok);
     if (bad != 0 && lane == 0) report_bad_blocks(a.err, int(__builtin_popcountll(bad)));
-    idw = (inside && ok) ? v : -1;
+    idw[h] = (inside && ok) ? v : -1;
   }
+  // id of entry e (wave-uniform) of the window
+  auto id_at = [&](int e) -> int32_t {
+    if constexpr (IDR == 1) return __builtin_amdgcn_readlane(idw[0], e);
+    else return e < 64 ? __builtin_amdgcn_readlane(idw[0], e) : __builtin_amdgcn_readlane(idw[1], e - 64);
+  };
   const unsigned char* zp = static_cast<const unsigned char*>(a.zero_page);
   auto blk_base = [&](const uint16_t* cache, int32_t blk) -> const uint16_t* {
     return blk < 0 ? reinterpret_cast<const uint16_t*>(zp) : cache + (int64_t(blk) * a.hkv + g) * (kBlockSize * D);
@@ -121,9 +130,9 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   // caches): measured 5.35 TB/s for the decode rows against 4.1 TB/s without it.
   auto load = [&](int jj, Tile& T) {
     const int kt = it.key_begin + jj * kSplitTile;
-    // tiles loaded past the wave's range may index past lane 63: any valid id will do
-    const int e = (2 * (jj - tw0)) & 63;
-    const int32_t s0 = __builtin_amdgcn_readlane(idw, e), s1 = __builtin_amdgcn_readlane(idw, e + 1);
+    // tiles loaded past the wave's range may index past the window: any valid id will do
+    const int e = (2 * (jj - tw0)) & (64 * IDR - 1);
+    const int32_t s0 = id_at(e), s1 = id_at(e + 1);
     const uint16_t* kb0 = blk_base(kc, s0);
     const uint16_t* kb1 = blk_base(kc, s1);
 #pragma unroll

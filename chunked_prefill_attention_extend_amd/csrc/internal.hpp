@@ -28,7 +28,8 @@ constexpr int kSplitRows = 16;    // split path: rows of one 16-row MFMA block
 constexpr int kSplitMaxRows = 32; // split path: at most this many rows (two blocks per wave)
 constexpr int kWideWaves = 4;      // wide-split kernel: wave64 per workgroup, one per SIMD, 512 registers each
 constexpr int kWideMaxRows = 64;   // ... at most this many rows per split item (four 16-row blocks per wave)
-constexpr int kWideKeysMax = 4096; // ... keys per workgroup: a wave's block ids fit one per lane
+constexpr int kWideKeysMax = 8192; // ... keys per workgroup: a wave's block ids fit two per lane
+constexpr int kWideTargetItems = 256;  // ... aims at this many workgroups
 // keys per split workgroup of `waves` waves, upper bound
 constexpr int split_keys_max(int waves) { return waves == kWideWaves ? kWideKeysMax : kSplitKeysMax; }
 constexpr int kFewRows = 2 * kRowsPerWave;  // chunk tiles of at most this many rows are cut into split-length key pieces

@@ -222,7 +222,8 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
     const int64_t split_max_rows = plan.wide ? kWideMaxRows : kSplitMaxRows;
     const int split_waves = plan.wide ? kWideWaves : kWaves;
     const int64_t kGrain = int64_t(kSplitTile) * split_waves;
-    int64_t piece = (split_keys + kSplitTargetItems - 1) / kSplitTargetItems;
+    const int64_t target = plan.wide ? kWideTargetItems : kSplitTargetItems;
+    int64_t piece = (split_keys + target - 1) / target;
     piece = (piece + kGrain - 1) / kGrain * kGrain;
     piece = std::min<int64_t>(std::max<int64_t>(piece, kSplitKeysMin), split_keys_max(split_waves));
     plan.split_keys = int32_t(piece);
