@@ -358,6 +358,34 @@ def test_invalid_block_ids_are_reported_not_read():
         ext.kv_append(kn, kn, cache.k, cache.v, bad, [16], [8], check=True)
 
 
+def test_invalid_block_ids_in_a_wide_split_launch():
+    """Verify rows of 48 rows per KV head (64 q / 8 kv heads, 6 tokens) run on the
+    4-wave wide-split kernel; an out-of-range block id there is read as zeros,
+    counted in the status words and raised with check=True, and the rows stay
+    finite."""
+    w = custom_workload(52, [(40, 6)], 64, 8, 128)
+    cache = PagedCache(w, fill=0.0)
+    r = w.requests[0]
+    cache.append([0], [0], w.k(r, 0, 46), w.v(r, 0, 46), [46])
+    bad = cache.bt.clone()
+    bad[0, 1] = w.num_blocks + 7
+    q = dev_tensor(w.q(r, 40, 46), w.dtype)
+    out = torch.empty_like(q)
+    nbytes = ext.workspace_bytes([40], [6], 64, 8, 128, ext.EXTATTN_BF16)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    _, st, _ = ext.extend_attention(q, cache.k, cache.v, bad, [40], [6], w.scale, out, None, workspace=ws,
+                                    timed=True)
+    torch.cuda.synchronize()
+    assert set(st[:, 2].cpu().numpy().tolist()) == {1}, "48 rows run as split items"
+    flags, count, _ = ext.read_status(ws)
+    assert flags == ext.STATUS_BAD_BLOCK and count > 0, f"status {flags:#x} / {count}"
+    assert torch.isfinite(out.float()).all()
+    with pytest.raises(ValueError, match="block id outside"):
+        ext.extend_attention(q, cache.k, cache.v, bad, [40], [6], w.scale, out, None, check=True)
+    ext.extend_attention(q, cache.k, cache.v, cache.bt, [40], [6], w.scale, out, None, workspace=ws)
+    assert ext.read_status(ws) == (0, 0, 0)
+
+
 def test_device_argument_errors():
     w = custom_workload(61, [(16, 16)], 8, 2, 128)
     cache = PagedCache(w, fill=0.0)

@@ -41,6 +41,8 @@ def test_noalloc_matches_the_workspace_entry_point():
     cases = [
         # a mixed launch: decode rows (split items and their combine), a chunk cut into key pieces
         ([(3000, 1), (6000, 700), (40, 1), (900, 5)], 32, 8, 128, 31),
+        # verify rows of 40-64 rows per KV head (the wide-split kernel), one context in two pieces
+        ([(9000, 8), (3000, 5), (50, 1)], 64, 8, 128, 34),
         # then a smaller one: fewer items, no pieces
         ([(100, 50)], 16, 4, 64, 32),
     ]
