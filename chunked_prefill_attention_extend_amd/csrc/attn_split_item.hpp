@@ -20,7 +20,8 @@ namespace extattn {
 // At 8 waves (256 registers a wave): with one row block two 32-key tiles are in
 // flight per wave; with two, the second block's operands take the registers of
 // the second tile, and the next tile is loaded as soon as the current one has
-// been consumed. At 4 waves (512 registers) a ring of 3-4 tiles.
+// been consumed. At 4 waves (512 registers) a ring of 4 tiles at up to two
+// blocks and of 2 at three or four.
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 

@@ -5,11 +5,11 @@
 // What is computed is the same as on the other kernels (zdszero "Chunked
 // Prefill" notes, section "prefill as several resumable extends": the softmax
 // of a query row over keys 0 .. its position, split key ranges merged by the
-// page's rule). Here a workgroup is 4 wave64, one per SIMD, each with 512
-// registers (half of them accumulation registers): a wave holds all of the
-// item's rows (four 16-row blocks sharing every K/V operand) and a ring of 3-4
-// K/V tiles, so the context is read once for up to 64 rows with ~200 KB of
-// loads in flight per CU.
+// page's rule). Here a workgroup is 4 wave64, one per SIMD, each with up to 512
+// registers (the output accumulators in the accumulation registers): a wave
+// holds all of the item's rows (one to four 16-row blocks sharing every K/V
+// operand) and a ring of K/V register tiles (4 at up to two blocks, 2 at three or
+// four), so the context is read once for up to 64 rows.
 #include "attn_split_item.hpp"
 
 namespace extattn {
