@@ -383,7 +383,11 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
   const int v_new = (si.prefix >> 5) - t0;
   const bool wait_new = a.n_append > 0 && v_new < n;
 
-  if (n > 0) {
+  // The loop is compiled twice: launches without fused appends get one with no
+  // wait code in its steps.
+  auto sweep = [&](auto fused_tag) {
+    constexpr bool FUSED = decltype(fused_tag)::value;
+    const bool wait_new_t = FUSED && wait_new;
     constexpr int kIssuePerStep = 2 * NINST;
     // Prologue: ids of windows 0 and 1; K of tiles t0 .. t0+KLEAD-1 and V of t0 ..
     // t0+VLEAD-1, each tile v in ring slot v % RING.
@@ -391,7 +395,7 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
     fill_ids(1);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     make_entries(0, -1);
-    if (wait_new && v_new < KLEAD) wait_appends_wave<WAVES>(a);
+    if (wait_new_t && v_new < KLEAD) wait_appends_wave<WAVES>(a);
 #pragma unroll
     for (int v = 0; v < KLEAD; ++v) issue_k(v, v);
 #pragma unroll
@@ -457,7 +461,7 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
         if ((u & 31) == 0 && u > 0) fill_ids((u >> 5) + 1);
       }
       auto issue = [&]() {
-        if (wait_new && u + KLEAD == v_new) wait_appends_wave<WAVES>(a);  // first copy of a new-key tile
+        if (wait_new_t && u + KLEAD == v_new) wait_appends_wave<WAVES>(a);  // first copy of a new-key tile
         issue_k(u + KLEAD, (sl + KLEAD) % RING);
         issue_v(u + VLEAD, (sl + VLEAD) % RING);
       };
@@ -569,6 +573,12 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
     for (; u < nfree; u += RING) group(F{}, u);
     for (; u < npad; u += RING) group(T{}, u);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
+  };
+  if (n > 0) {
+    if (wait_new)
+      sweep(std::true_type{});
+    else
+      sweep(std::false_type{});
   }
   if (!ovf) {
 #pragma unroll
