@@ -188,6 +188,13 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
       if constexpr (RB == 2) asm volatile("" : "+a"(qf[b][ks]));
     }
   }
+  // Q's loads are waited for here, once: otherwise the compiler waits for them at
+  // their first use in every step (each step's products sit under a branch), and
+  // such a wait (vmcnt 0) also drains the tile copies in flight.
+  if constexpr (RB == 1) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[0][ks]));
+  }
   const int lim_min = min(si.prefix + it.row0 / G, it.key_end - 1);
 
   const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
