@@ -382,9 +382,7 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
   if (workspace_bytes < plan.bytes)
     return fail(EXTATTN_ENOSPC, "workspace too small: the launch needs " + std::to_string(plan.bytes) + " bytes, " +
                                     std::to_string(workspace_bytes) + " available");
-  // the plan lists the fused append's items first; a plain launch starts after them
-  const int32_t first = fused ? 0 : plan.n_append;
-  const int32_t n_launch = int32_t(plan.items.size()) - first;
+  const int32_t n_launch = int32_t(plan.items.size());
   if (timed) {
     if (!n_items || !tick_hz) return fail(EXTATTN_EINVAL, "null n_items or tick_hz");
     if (dtype != EXTATTN_BF16) return fail(EXTATTN_EUNSUPPORTED, "timed launches exist for bf16 only");
@@ -411,7 +409,7 @@ int extend_call(const void* q, const void* k_cache, const void* v_cache, const i
   a.out = out;
   a.lse = lse;
   a.seqs = reinterpret_cast<const SeqInfo*>(ws + plan.off_seqs);
-  a.items = reinterpret_cast<const WorkItem*>(ws + plan.off_items) + first;
+  a.items = reinterpret_cast<const WorkItem*>(ws + plan.off_items);
   a.tasks = reinterpret_cast<const CombineTask*>(ws + plan.off_tasks);
   a.slots = reinterpret_cast<float*>(ws + plan.off_slots);
   a.err = reinterpret_cast<int32_t*>(ws);

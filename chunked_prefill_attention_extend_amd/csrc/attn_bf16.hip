@@ -43,9 +43,8 @@ void attn_bf16_kernel(AttnArgs a) {
     st[2] = it.kind;
     st[3] = it.seq;
   }
-  if (it.kind == kItemAppend) {
-    append_item<D, kWaves>(a, it);
-  } else if (it.kind == kItemChunk) {
+  if (a.n_append > 0 && int(blockIdx.x) < a.n_append) append_share<D, kWaves>(a, blockIdx.x);
+  if (it.kind == kItemChunk) {
     chunk_item_t<D, 1, kWaves>(a, it, smem);  // waits for the appends before its first new-key copy
   } else {
     if (a.n_append > 0 && it.key_end > a.seqs[it.seq].prefix) wait_appends<kWaves>(a);  // reads new keys

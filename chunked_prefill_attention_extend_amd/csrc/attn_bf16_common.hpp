@@ -139,46 +139,127 @@ __device__ inline void dma4(const void* base, uint32_t off, uint32_t lds) {
 constexpr float kSumBound = 4096.0f;
 
 // ---------------------------------------------------------------------------
-// Fused append. Append items copy new tokens of one request from k_new / v_new
-// into the paged cache (K as one 16-byte store per piece, V scattered into the
-// slot-minor layout), then each wave adds 1 to the completion counter with
-// release semantics at device scope. An attention item whose key range reaches
-// the request's new keys waits, before its first load, until the counter says
-// that every append wave is done. The append items lead the launch order and
-// every die dispatches its workgroups in order, so the waits end; the wait is
-// still bounded and sets kStatusWaitTimeout in the status flags if it gives up.
+// Fused append. Workgroup p < n_append of the launch first copies groups
+// [p NG / n_append, (p+1) NG / n_append) of the NG groups of 16 consecutive new
+// tokens of the launch (rows of k_new, request order) into the paged cache: K as
+// 16-byte pieces, V as whole 16-slot rows of the slot-minor layout when the group
+// fills one cache block (else element by element); then each of its waves adds 1 to
+// the completion counter with release semantics at device scope, and the
+// workgroup goes on to its own work item. Work that reads new keys waits until
+// the counter says that every copying wave is done. The copying workgroups are
+// the first of the launch, so every die dispatches its share of them before any
+// other workgroup of the launch, and they wait for nothing before they signal: the
+// waits end. A wait is still bounded and sets kStatusWaitTimeout in the status
+// flags if it gives up.
 // ---------------------------------------------------------------------------
 template <int D, int WAVES>
-__device__ void append_item(const AttnArgs& a, const WorkItem& it) {
+__device__ void append_share(const AttnArgs& a, int p) {
   constexpr int PIECES = D / 8;  // 16-byte pieces of a head vector
-  const SeqInfo si = a.seqs[it.seq];
-  const int per_tok = a.hkv * PIECES;
-  const int n = it.nrows * per_tok;
-  const int32_t* bt = a.block_table + int64_t(it.seq) * a.max_blocks;
-  for (int i = threadIdx.x; i < n; i += 64 * WAVES) {
-    const int t = i / per_tok;
-    const int rem = i - t * per_tok;
-    const int g = rem / PIECES, c = rem - g * PIECES;
-    const int tok = it.row0 + t;  // new token index within the request
-    const int pos = si.prefix + tok;
-    const int32_t phys = bt[pos / kBlockSize];
-    if (!block_ok(phys, a.num_blocks)) {
-      if (g == 0 && c == 0) report_bad_blocks(a.err, 1);
-      continue;
-    }
-    const int slot = pos % kBlockSize;
-    const int64_t src = (int64_t(si.q_off + tok) * a.hkv + g) * D + c * 8;
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k_new) + src);
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v_new) + src);
-    uint16_t* kc = static_cast<uint16_t*>(a.k_cache_w) + ((int64_t(phys) * a.hkv + g) * kBlockSize + slot) * D + c * 8;
-    *reinterpret_cast<u32x4*>(kc) = kv;
-    uint16_t* vc = static_cast<uint16_t*>(a.v_cache_w) + (int64_t(phys) * a.hkv + g) * int64_t(D) * kBlockSize +
-                   int64_t(c * 8) * kBlockSize + slot;
+  constexpr int NT = 64 * WAVES;
+  const int tid = threadIdx.x;
+  const int total = a.total_rows;
+  // whole groups of 16 consecutive new tokens (rows of k_new): groups [gb, ge)
+  const int ngroups = (total + kBlockSize - 1) / kBlockSize;
+  const int gb = int(int64_t(ngroups) * p / a.n_append), ge = int(int64_t(ngroups) * (p + 1) / a.n_append);
+  const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
+  const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
+  uint16_t* kc = static_cast<uint16_t*>(a.k_cache_w);
+  uint16_t* vc = static_cast<uint16_t*>(a.v_cache_w);
+  const int hkv = a.hkv;
+  // physical block and slot of new-token row t (-1: invalid block id, reported once per token)
+  auto locate = [&](int t, int& slot) -> int32_t {
+    const int r = find_seq(a.seqs, a.num_seqs, t);
+    const SeqInfo si = a.seqs[r];
+    const int pos = si.prefix + (t - si.q_off);
+    slot = pos % kBlockSize;
+    return a.block_table[int64_t(r) * a.max_blocks + pos / kBlockSize];
+  };
+  constexpr int KB = 4;  // K pieces, and V rows / 2, a thread loads before it stores
+  for (int grp = gb; grp < ge; ++grp) {
+    const int t0 = grp * kBlockSize;
+    const int nt = min(kBlockSize, total - t0);
+    const int nk = nt * hkv * PIECES, nv = hkv * D;
+    // The first batch of the group's K pieces and V rows is loaded before the
+    // block lookup, so that the loads overlap the lookup's dependent reads.
+    u32x4 kv[KB];
+    uint32_t vw[2][kBlockSize / 2];
+    auto load_k = [&](int base) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t w = vv[e];
-      vc[(2 * e) * kBlockSize] = uint16_t(w & 0xFFFFu);
-      vc[(2 * e + 1) * kBlockSize] = uint16_t(w >> 16);
+      for (int k = 0; k < KB; ++k) {
+        const int i = base + k * NT;
+        if (i < nk) {
+          const int tl = i / (hkv * PIECES), rem = i - tl * (hkv * PIECES);
+          kv[k] = *reinterpret_cast<const u32x4*>(kn + (int64_t(t0 + tl) * hkv + rem / PIECES) * D + (rem % PIECES) * 8);
+        }
+      }
+    };
+    auto load_v = [&](int base) {  // the group's 16 tokens of (head, feature) rows base, base + NT
+      if (nt < kBlockSize) return;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int i = base + k * NT;
+        if (i < nv) {
+          const int g = i / D, d = i - g * D;
+#pragma unroll
+          for (int e = 0; e < kBlockSize / 2; ++e)
+            vw[k][e] = uint32_t(vn[(int64_t(t0 + 2 * e) * hkv + g) * D + d]) |
+                       (uint32_t(vn[(int64_t(t0 + 2 * e + 1) * hkv + g) * D + d]) << 16);
+        }
+      }
+    };
+    load_k(tid);
+    load_v(tid);
+    // the usual case: the group's tokens are slots 0..15 of one cache block
+    const int r0 = find_seq(a.seqs, a.num_seqs, t0);
+    const SeqInfo s0 = a.seqs[r0];
+    const int pos0 = s0.prefix + (t0 - s0.q_off);
+    const bool whole = nt == kBlockSize && t0 + kBlockSize <= s0.q_off + s0.extend && pos0 % kBlockSize == 0;
+    const int32_t phys0 = whole ? a.block_table[int64_t(r0) * a.max_blocks + pos0 / kBlockSize] : -1;
+    const bool whole_ok = whole && block_ok(phys0, a.num_blocks);
+    // K: one 16-byte piece per (token, head, piece)
+    for (int base = tid; base < nk; base += KB * NT) {
+      if (base != tid) load_k(base);
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int i = base + k * NT;
+        if (i >= nk) continue;
+        const int tl = i / (hkv * PIECES), rem = i - tl * (hkv * PIECES);
+        const int g = rem / PIECES, c = rem % PIECES;
+        int slot = tl;
+        const int32_t phys = whole ? phys0 : locate(t0 + tl, slot);
+        if (!block_ok(phys, a.num_blocks)) {
+          if (g == 0 && c == 0) report_bad_blocks(a.err, 1);
+          continue;
+        }
+        *reinterpret_cast<u32x4*>(kc + ((int64_t(phys) * hkv + g) * kBlockSize + slot) * D + c * 8) = kv[k];
+      }
+    }
+    // V (slot-minor): whole 16-slot rows of the block, else element by element
+    for (int base = tid; base < nv; base += 2 * NT) {
+      if (whole) {
+        if (base != tid) load_v(base);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int i = base + k * NT;
+          if (i >= nv || !whole_ok) continue;  // invalid ids were reported with K
+          const int g = i / D, d = i - g * D;
+          u32x4* dst = reinterpret_cast<u32x4*>(vc + ((int64_t(phys0) * hkv + g) * D + d) * kBlockSize);
+          dst[0] = u32x4{vw[k][0], vw[k][1], vw[k][2], vw[k][3]};
+          dst[1] = u32x4{vw[k][4], vw[k][5], vw[k][6], vw[k][7]};
+        }
+      } else {
+        for (int k = 0; k < 2; ++k) {
+          const int i = base + k * NT;
+          if (i >= nv) continue;
+          const int g = i / D, d = i - g * D;
+          for (int tl = 0; tl < nt; ++tl) {
+            int slot;
+            const int32_t phys = locate(t0 + tl, slot);
+            if (!block_ok(phys, a.num_blocks)) continue;
+            vc[((int64_t(phys) * hkv + g) * D + d) * kBlockSize + slot] = vn[(int64_t(t0 + tl) * hkv + g) * D + d];
+          }
+        }
+      }
     }
   }
   if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(a.append_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);

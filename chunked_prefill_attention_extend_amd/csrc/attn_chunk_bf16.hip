@@ -1,4 +1,4 @@
-// bf16 extend attention for launches of chunk rows only (and their fused appends):
+// bf16 extend attention for launches of chunk rows only (with a fused append or not):
 // one workgroup of 8 waves per chunk item (attn_chunk_item.hpp), no decode / verify
 // items, so the kernel holds only the chunk code.
 #include "attn_chunk_item.hpp"
@@ -18,11 +18,8 @@ void chunk_bf16_kernel(AttnArgs a) {
     st[2] = it.kind;
     st[3] = it.seq;
   }
-  if (it.kind == kItemAppend) {
-    append_item<D, WAVES>(a, it);
-  } else {
-    chunk_item_t<D, RB, WAVES>(a, it, smem);  // waits for the appends before its first new-key copy
-  }
+  if (a.n_append > 0 && int(blockIdx.x) < a.n_append) append_share<D, WAVES>(a, blockIdx.x);
+  chunk_item_t<D, RB, WAVES>(a, it, smem);  // waits for the appends before its first new-key copy
   if (a.stamps) {
     __syncthreads();
     if (threadIdx.x == 0) {

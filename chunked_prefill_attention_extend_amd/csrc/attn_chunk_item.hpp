@@ -383,18 +383,19 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
     }
   };
 
-  // Fused append: the launch's append items write the new tokens' K/V (keys P and
-  // up) into the cache. Tiles below tile P / 32 hold only older keys, in whole cache
+  // Fused append: the launch's first workgroups write the new tokens' K/V (keys P
+  // and up) into the cache. Tiles below tile P / 32 hold only older keys, in whole cache
   // blocks the appends never touch, so a wave waits for the appends only before it
   // copies tile P / 32 (relative index v_new), if that tile is in its range.
   const int v_new = (si.prefix >> 5) - t0;
   const bool wait_new = a.n_append > 0 && v_new < n;
 
-  // The loop is compiled twice: launches without fused appends get one with no
-  // wait code in its steps.
+  // The wave waits once, at the start of the 8-step group whose steps issue that
+  // copy (the prologue, when the copy is among the first KLEAD), so the steps hold
+  // no test for it; launches without fused appends run a copy of the loop without
+  // the group test.
   auto sweep = [&](auto fused_tag) {
     constexpr bool FUSED = decltype(fused_tag)::value;
-    const bool wait_new_t = FUSED && wait_new;
     constexpr int kIssuePerStep = 2 * NINST;
     // Prologue: ids of windows 0 and 1; K of tiles t0 .. t0+KLEAD-1 and V of t0 ..
     // t0+VLEAD-1, each tile v in ring slot v % RING.
@@ -402,7 +403,8 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
     fill_ids(1);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     make_entries(0, -1);
-    if (wait_new_t && v_new < KLEAD) wait_appends_wave<WAVES>(a);
+    if (FUSED && v_new < KLEAD) wait_appends_wave<WAVES>(a);
+    bool wait_pending = FUSED && v_new >= KLEAD;
 #pragma unroll
     for (int v = 0; v < KLEAD; ++v) issue_k(v, v);
 #pragma unroll
@@ -468,7 +470,6 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
         if ((u & 31) == 0 && u > 0) fill_ids((u >> 5) + 1);
       }
       auto issue = [&]() {
-        if (wait_new_t && u + KLEAD == v_new) wait_appends_wave<WAVES>(a);  // first copy of a new-key tile
         issue_k(u + KLEAD, (sl + KLEAD) % RING);
         issue_v(u + VLEAD, (sl + VLEAD) % RING);
       };
@@ -576,9 +577,22 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
       step(std::integral_constant<int, 7>{}, mask_tag, u + 7, sb, sa, pb, pa, lb, la);
     };
     static_assert(RING == 8, "the loop body runs RING steps");
+    // before a group whose steps copy tile v_new (step v_new - KLEAD) or later tiles
+    auto wait_before = [&](int u) {
+      if (FUSED && wait_pending && v_new < u + RING + KLEAD) {
+        wait_appends_wave<WAVES>(a);
+        wait_pending = false;
+      }
+    };
     int u = 0;
-    for (; u < nfree; u += RING) group(F{}, u);
-    for (; u < npad; u += RING) group(T{}, u);
+    for (; u < nfree; u += RING) {
+      wait_before(u);
+      group(F{}, u);
+    }
+    for (; u < npad; u += RING) {
+      wait_before(u);
+      group(T{}, u);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the copies issued past the end
   };
   if (n > 0) {

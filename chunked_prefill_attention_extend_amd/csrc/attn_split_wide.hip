@@ -28,19 +28,16 @@ void split_wide_kernel(AttnArgs a) {
     st[2] = it.kind;
     st[3] = it.seq;
   }
-  if (it.kind == kItemAppend) {
-    append_item<D, kWideWaves>(a, it);
-  } else {
-    if (a.n_append > 0 && it.key_end > a.seqs[it.seq].prefix) wait_appends<kWideWaves>(a);  // reads new keys
-    if (it.nrows <= 16)
-      split_item<D, 1, kWideWaves>(a, it, smem);
-    else if (it.nrows <= 32)
-      split_item<D, 2, kWideWaves>(a, it, smem);
-    else if (it.nrows <= 48)
-      split_item<D, 3, kWideWaves>(a, it, smem);
-    else
-      split_item<D, 4, kWideWaves>(a, it, smem);
-  }
+  if (a.n_append > 0 && int(blockIdx.x) < a.n_append) append_share<D, kWideWaves>(a, blockIdx.x);
+  if (a.n_append > 0 && it.key_end > a.seqs[it.seq].prefix) wait_appends<kWideWaves>(a);  // reads new keys
+  if (it.nrows <= 16)
+    split_item<D, 1, kWideWaves>(a, it, smem);
+  else if (it.nrows <= 32)
+    split_item<D, 2, kWideWaves>(a, it, smem);
+  else if (it.nrows <= 48)
+    split_item<D, 3, kWideWaves>(a, it, smem);
+  else
+    split_item<D, 4, kWideWaves>(a, it, smem);
   if (a.stamps) {
     __syncthreads();
     if (threadIdx.x == 0) {

@@ -45,14 +45,16 @@ struct SeqInfo {
 enum : int32_t {
   kItemChunk = 0,  // kRowsPerTile rows of one (request, KV head); all waves share LDS K/V tiles
   kItemSplit = 1,  // <= kSplitMaxRows rows (kWideMaxRows in wide launches); each wave takes its own part of the key range
-  kItemAppend = 2, // fused append: copy new tokens [row0, row0 + nrows) of a request into the cache
 };
 
 // Measurement variant: one record per work item, {start, end} in wall-clock ticks,
 // {kind, request}, {start, end} in shader-clock cycles.
 constexpr int kStampWords = 6;
 
-constexpr int kAppendTokens = 16;  // tokens per append item of a fused append + attention launch
+// Fused append + attention launches: the first min(items, kAppendProducers) workgroups
+// each copy an equal share of the launch's new tokens into the cache before their own
+// work item (8 a die with the round-robin deal of workgroups to the 8 dies).
+constexpr int kAppendProducers = 64;
 constexpr int kAppendDoneOffset = 128;  // byte offset of the append completion counter in the workspace header
 // Status words at the start of the workspace (reset by every call's metadata upload):
 // word 0 holds flags, word 1 counts invalid block-id reads (wrapping), word 2 counts
@@ -121,9 +123,9 @@ struct AttnArgs {
   int32_t n_items;
   int32_t n_tasks;
   int64_t* stamps;   // NULL, or [n_items][kStampWords] {start, end, kind, request, clk_start, clk_end}
-  // fused append (n_append > 0): the first n_append items copy k_new / v_new
-  // [sum(E), Hkv, D] into the cache; every wave of them adds 1 to *append_done
-  // (release), and attention items that read new keys wait for n_append * kWaves
+  // fused append (n_append > 0): workgroups 0 .. n_append-1 first copy their share
+  // of k_new / v_new [sum(E), Hkv, D] into the cache, then every wave of them adds 1
+  // to *append_done (release); work that reads new keys waits for n_append * waves
   const void* k_new;
   const void* v_new;
   void* k_cache_w;
@@ -155,7 +157,7 @@ struct Plan {
   std::vector<CombineTask> tasks;
   int64_t n_slot_floats = 0;  // size of the partial-slot area
   int32_t split_keys = 0;  // keys per split workgroup (0: no split items)
-  int32_t n_append = 0;    // append items at the head of `items` (fused append launch)
+  int32_t n_append = 0;    // workgroups that also copy new tokens in a fused append launch
   int32_t n_split = 0;     // split items (decode / verify rows) in `items`
   bool wide = false;       // every split item runs on the 4-wave wide-split kernel (up to kWideMaxRows rows)
   int64_t total_rows = 0;
@@ -222,8 +224,8 @@ int decode_first_with_slack_impl(int64_t ready_decode, int64_t pending_prefill, 
 
 // kernel launchers (one per .hip file)
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_chunk_bf16(const AttnArgs& a, hipStream_t stream);  // chunk and append items only
-hipError_t launch_split_wide(const AttnArgs& a, hipStream_t stream);  // split and append items only
+hipError_t launch_chunk_bf16(const AttnArgs& a, hipStream_t stream);  // chunk items only
+hipError_t launch_split_wide(const AttnArgs& a, hipStream_t stream);  // split items only
 hipError_t launch_combine(const AttnArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const KvArgs& a, int32_t dtype, hipStream_t stream);

@@ -314,15 +314,19 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
     }
     order_items(groups, split_items, plan.items);
     if (with_append) {
-      // Fused append: the copies of the new tokens come first in the launch, so
-      // every die dispatches them before any attention item that waits for them.
-      std::vector<WorkItem> app;
-      for (int32_t r = 0; r < num_seqs; ++r)
-        for (int32_t t = 0; t < extend[r]; t += kAppendTokens)
-          app.push_back(WorkItem{kItemAppend, r, 0, t, std::min(kAppendTokens, extend[r] - t), 0, 0, -1, -1, 0,
-                                 {0, 0}});
-      plan.n_append = int32_t(app.size());
-      plan.items.insert(plan.items.begin(), app.begin(), app.end());
+      // Fused append: the launch's first workgroups (the heads of every die's
+      // dispatch order) copy the new tokens before their own items, so every die
+      // dispatches them before any work that waits for them.
+      plan.n_append = int32_t(std::min<size_t>(plan.items.size(), kAppendProducers));
+      // A launch of at most one workgroup per CU runs all its items at once, so
+      // their order in a lane does not matter for the balance: reversed, each
+      // lane starts with its shortest items, which then also copy the new tokens.
+      const size_t n = plan.items.size();
+      if (n <= size_t(kChunkTargetItems))
+        for (size_t l = 0; l < size_t(kXcds) && l < n; ++l) {
+          size_t lo = l, hi = l + (n - 1 - l) / kXcds * kXcds;
+          for (; lo < hi; lo += kXcds, hi -= kXcds) std::swap(plan.items[lo], plan.items[hi]);
+        }
     }
   }
 

@@ -3,9 +3,9 @@
 Builds tests/plan_check.cpp against the library's planner source with g++ and the
 address and undefined-behaviour sanitizers, and runs it: every row's keys covered
 exactly once by the work list, split key ranges merged exactly once over written
-partial slots, slots disjoint, split pieces within the per-wave id budget, fused
-append items first and covering every new token once, each chunk group on a
-contiguous run of die lanes. Builds tests/plan_cache_check.cpp the same way, and
+partial slots, slots disjoint, split pieces within the per-wave id budget, the
+fused append's copying workgroups counted, each chunk group on a contiguous run
+of die lanes. Builds tests/plan_cache_check.cpp the same way, and
 once more under the thread sanitizer for its many-thread lookups: cached records
 equal fresh plans, keys tell every shape apart, least-recently-used eviction and
 the bounds hold.
