@@ -154,21 +154,26 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       f32x4 sc[2];
+      // With Q in LDS, block rb's KS operand pieces are read together, once per
+      // tile, before its products (an opaque address: the compiler must not hoist
+      // the reads out of the loop into registers).
+      u32x4 qq[KS];
+      if constexpr (QLDS) {
+        uint32_t qa = qimg + uint32_t((rb * KS * 64 + lane) * 16);
+        asm volatile("" : "+v"(qa));
+        typedef __attribute__((address_space(3))) const u32x4 lds_cq_t;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qq[ks] = *reinterpret_cast<lds_cq_t*>(qa + uint32_t(ks * 64 * 16));
+      }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          if constexpr (QLDS) {
-            // an opaque address per tile: the compiler must not hoist these reads
-            // out of the loop into registers
-            uint32_t qa = qimg + uint32_t(((rb * KS + ks) * 64 + lane) * 16);
-            asm volatile("" : "+v"(qa));
-            typedef __attribute__((address_space(3))) const u32x4 lds_cq_t;
-            sc[b] = mfma16(T.kf[b][ks], *reinterpret_cast<lds_cq_t*>(qa), sc[b]);
-          } else {
+          if constexpr (QLDS)
+            sc[b] = mfma16(T.kf[b][ks], qq[ks], sc[b]);
+          else
             sc[b] = mfma16(T.kf[b][ks], qf[rb][ks], sc[b]);
-          }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
