@@ -151,19 +151,26 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   auto compute = [&](Tile& T) {
     const int kt = T.kt;
     u32x4 pf[RB];
+    // With Q in LDS, a block's KS operand pieces are read together, once per tile,
+    // the next block's while this block's products run (an opaque address: the
+    // compiler must not hoist the reads out of the loop into registers).
+    u32x4 qn[KS];
+    auto read_q = [&](int rb) {
+      uint32_t qa = qimg + uint32_t((rb * KS * 64 + lane) * 16);
+      asm volatile("" : "+v"(qa));
+      typedef __attribute__((address_space(3))) const u32x4 lds_cq_t;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qn[ks] = *reinterpret_cast<lds_cq_t*>(qa + uint32_t(ks * 64 * 16));
+    };
+    if constexpr (QLDS) read_q(0);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       f32x4 sc[2];
-      // With Q in LDS, block rb's KS operand pieces are read together, once per
-      // tile, before its products (an opaque address: the compiler must not hoist
-      // the reads out of the loop into registers).
       u32x4 qq[KS];
       if constexpr (QLDS) {
-        uint32_t qa = qimg + uint32_t((rb * KS * 64 + lane) * 16);
-        asm volatile("" : "+v"(qa));
-        typedef __attribute__((address_space(3))) const u32x4 lds_cq_t;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qq[ks] = *reinterpret_cast<lds_cq_t*>(qa + uint32_t(ks * 64 * 16));
+        for (int ks = 0; ks < KS; ++ks) qq[ks] = qn[ks];
+        if (rb + 1 < RB) read_q(rb + 1);
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
