@@ -63,6 +63,10 @@ def _run_both(w):
     ([(777, 40), (33, 1), (0, 17)], 16, 2, 64, "bf16"),  # D=64
     ([(3000, 5), (4000, 8), (12, 1), (9000, 7)], 64, 8, 128, "bf16"),  # 40-64 verify rows: wide kernel
     ([(50, 30), (129, 1)], 8, 2, 128, "f32"),  # fp32: append launch, then attention
+    # copying workgroups take several 16-token groups each, none of them one whole cache
+    # block (the prefix ends inside a block), the last group shared by two requests
+    ([(37, 6003), (5000, 1)], 32, 8, 128, "bf16"),
+    ([(40, 16)], 8, 8, 128, "bf16"),        # 8 work items, so 8 copying workgroups, 7 of them idle
 ])
 def test_fused_append_matches_separate(case):
     launches, hq, hkv, d, dt = case
