@@ -27,6 +27,9 @@ ARCH = "gfx950"
 HIP_FLAGS = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the iterative ILP scheduler: measured +0.5% on the chunk kernel, +2-3% on the
+    # split kernels' verify rows of 20-64 rows per KV head, against the default
+    "-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
     "-I", os.path.join(ROOT, "include"),
 ]
 CXX_FLAGS = [
