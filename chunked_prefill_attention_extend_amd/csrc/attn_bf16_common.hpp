@@ -133,10 +133,6 @@ __device__ inline void dma4(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
 }
 
-// Bound on one lane's row sum of a chunk tile's 16 weights. Below it every weight is
-// at most 2^12, so O and l stay far from fp32 overflow; above it (or when a weight
-// overflowed to inf) the running max is raised before the weights are used.
-constexpr float kSumBound = 4096.0f;
 
 // ---------------------------------------------------------------------------
 // Fused append. Workgroup p < n_append of the launch first copies groups
