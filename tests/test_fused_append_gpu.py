@@ -124,7 +124,7 @@ def test_fused_append_invalid_block_ids_are_reported_not_written():
         ext.extend_attention_append(q, kn, vn, fus.k, fus.v, bad, [40], [24], w.scale, out, None)
 
 
-@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_fused_append_random_launches(seed):
     """Random mixed launches through the fused path: caches, out and lse bit for bit
     as kv_append followed by extend_attention."""
