@@ -450,7 +450,7 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
     //     j+1's weights (masked if diagonal; packed and summed one slot later, into
     //     py / lsy),
     //   issues the copies of K(j+KLEAD) (slot last read in step u-2) and V(j+VLEAD)
-    //     (slot last read in step u+VLEAD-8) half way,
+    //     (slot last read in step u+VLEAD-8) after its first interleave slot,
     //   and, after odd steps only, waits for the copies issued up to step u-OUT and
     //     meets the other waves. Between a slot's last read and its next copy, and
     //     between a copy and its first read, lie at least one such barrier (see OUT).
@@ -541,7 +541,7 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
 #pragma unroll
               for (int q = 0; q < PPS; ++q) finish(b, (t - 1) * PPS + q);
           }
-          if (t == KS / 2 - 1) issue();
+          if (t == 0) issue();  // the step's copies go out after its first slot
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
