@@ -450,7 +450,8 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
     //     j+1's weights (masked if diagonal; packed and summed one slot later, into
     //     py / lsy),
     //   issues the copies of K(j+KLEAD) (slot last read in step u-2) and V(j+VLEAD)
-    //     (slot last read in step u+VLEAD-8) after its first interleave slot,
+    //     (slot last read in step u+VLEAD-8) after its first and second interleave
+    //     slots,
     //   and, after odd steps only, waits for the copies issued up to step u-OUT and
     //     meets the other waves. Between a slot's last read and its next copy, and
     //     between a copy and its first read, lie at least one such barrier (see OUT).
@@ -469,11 +470,12 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
         if ((u & 31) == 16 - KLEAD && u >= 48 - KLEAD) make_entries((u + KLEAD) >> 5, 1);
         if ((u & 31) == 0 && u > 0) fill_ids((u >> 5) + 1);
       }
-      auto issue = [&]() {
-        issue_k(u + KLEAD, (sl + KLEAD) % RING);
-        issue_v(u + VLEAD, (sl + VLEAD) % RING);
-      };
-      if (!wave_rows) issue();
+      auto issue_kc = [&]() { issue_k(u + KLEAD, (sl + KLEAD) % RING); };
+      auto issue_vc = [&]() { issue_v(u + VLEAD, (sl + VLEAD) % RING); };
+      if (!wave_rows) {
+        issue_kc();
+        issue_vc();
+      }
       if (wave_rows) {
         check(lsx);
         // In the masked steps (tile j+1 at or past j_mask), weights of keys past a row's
@@ -541,7 +543,9 @@ __device__ void chunk_item_t(const AttnArgs& a, const WorkItem& it, unsigned cha
 #pragma unroll
               for (int q = 0; q < PPS; ++q) finish(b, (t - 1) * PPS + q);
           }
-          if (t == 0) issue();  // the step's copies go out after its first slot
+          // the step's copies go out after its first two slots, K then V
+          if (t == 0) issue_kc();
+          if (t == 1) issue_vc();
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
