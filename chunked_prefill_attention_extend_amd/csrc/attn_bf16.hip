@@ -12,10 +12,10 @@
 //    whole GQA group shares each K/V read.
 //  * Chunk items run the shared chunk code (attn_chunk_item.hpp).
 //  * Split items (<= 32 rows: decode rows, multi-token verify rows): every
-//    wave takes all the rows and reads its own part of the key range straight
-//    from HBM into MFMA operand registers (no LDS); the waves' parts are merged
-//    in LDS, and a workgroup whose range is part of a longer context leaves a
-//    partial result for the combine kernel.
+//    wave takes all the rows and streams its own part of the key range through
+//    an LDS slot of its own (whole-line copies, one tile ahead); the waves'
+//    parts are merged in LDS, and a workgroup whose range is part of a longer
+//    context leaves a partial result for the combine kernel.
 //
 // Both paths contract on the matrix cores with the key order inside a 32-key
 // block permuted so that each lane's P^T values cover consecutive keys, which
@@ -33,6 +33,7 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int kChunkLds = 2 * kChunkRing * kChunkKeys * D * 2 + 512;            // K/V rings + block ids
   constexpr int kSplitLds = kWaves * 2 * kSplitRows * (D + 2) * 4;                 // wave partials (2 row blocks)
   __shared__ __attribute__((aligned(16))) unsigned char smem[kChunkLds > kSplitLds ? kChunkLds : kSplitLds];
+  static_assert(split_slot_lds<D>() <= (kChunkLds > kSplitLds ? kChunkLds : kSplitLds), "split tile slots fit");
   const WorkItem it = a.items[blockIdx.x];
   // measurement variant: the workgroup's start and end (after its last wave) in
   // wall-clock ticks; the start is stored at once so that nothing stays live

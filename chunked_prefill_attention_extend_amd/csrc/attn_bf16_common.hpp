@@ -129,6 +129,12 @@ __device__ inline uint32_t lds_addr(const void* p) {
 __device__ inline void dma16(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
 }
+// The same copy with the non-temporal hint, for bytes read exactly once (split
+// items): streamed past the caches, 6.9 against 6.1 TB/s for whole-line copies with
+// all CUs reading, 55 against 52 GB/s per CU with 64.
+__device__ inline void dma16_nt(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
+}
 __device__ inline void dma4(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
 }

@@ -1,6 +1,6 @@
 // Split items of the bf16 path: decode rows and multi-token verify rows, each
-// wave streaming its own part of the key range from HBM into MFMA operand
-// registers (shared by the mixed kernel and the 4-wave wide-split kernel).
+// wave streaming its own part of the key range from HBM (shared by the mixed
+// kernel and the 4-wave wide-split kernel).
 #pragma once
 
 #include "attn_bf16_common.hpp"
@@ -10,18 +10,23 @@ namespace extattn {
 // ---------------------------------------------------------------------------
 // Split items: <= 32 rows on the 8-wave kernels, <= 64 on the 4-wave wide-split
 // kernel (decode rows, multi-token verify rows); each of the W waves streams its
-// own part of the key range from HBM straight into MFMA operand registers. These
+// own part of the key range from HBM. These
 // run on v_mfma_f32_16x16x32_bf16 with RB = 1 .. 4 blocks of 16 query rows per
 // wave; the RB blocks share every K/V operand, so the context is read once
 // whatever the row count. Accumulator element i of lane l belongs to
 // query row l % 16 of its block and MFMA row 4 (l / 16) + i; MFMA row r of key
 // block b holds key 8 (r / 4) + 4 b + r % 4 of the tile, so each lane's P^T
 // operand (4 values from block 0, 4 from block 1) covers 8 consecutive keys.
-// At 8 waves (256 registers a wave): with one row block two 32-key tiles are in
-// flight per wave; with two, the second block's operands take the registers of
-// the second tile, and the next tile is loaded as soon as the current one has
-// been consumed. At 4 waves (512 registers) a ring of 4 tiles at up to two
-// blocks and of 2 at three or four.
+// At 8 waves (256 registers a wave) each wave copies its next 32-key tile (K and
+// V, 16 KB at D = 128) whole into an LDS slot of its own while the current one is
+// computed, and reads it back in operand layout. Loaded straight into operand
+// registers, a K operand instruction would read 64 bytes of each of 16 keys: half
+// of 16 cache lines per instruction, which streams at about half the rate of whole
+// lines (27 against 52 GB/s per CU with 64 CUs reading, 5.9 against 6.8 TB/s with
+// all of them). The copies read whole lines: 4 keys x 256 B of K or 32 feature rows
+// x 32 B of V per instruction, with the non-temporal hint (every byte is read
+// once). At 4 waves (512 registers) K and V go straight into
+// a register ring of 4 tiles at up to two row blocks and of 2 at three or four.
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -29,6 +34,22 @@ __device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                  c, 0, 0, 0);
 }
+
+// Position XOR of the 16-byte pieces of key k (0..31) in a split tile's K rows in
+// LDS. The 16 keys one operand read touches (MFMA row r holds key 8 (r / 4) + r % 4
+// + 4 b) get 16 distinct values at D = 128 (256-byte rows: the value is r), and at
+// D = 64 (128-byte rows, two to a 256-byte bank row) 8 distinct values among the
+// keys of either parity, so each 16-lane group of a read hits 16 different bank
+// groups.
+template <int D>
+__device__ constexpr int kswz(int k) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  return D == 128 ? ((k & 3) | (((k >> 3) & 3) << 2)) : (((k >> 1) & 1) | (((k >> 3) & 3) << 1));
+}
+
+// LDS bytes of the 8-wave split path's tile slots (K and V of one 32-key tile a wave).
+template <int D>
+constexpr int split_slot_lds() { return kWaves * 2 * kSplitTile * D * 2; }
 
 template <int D, int RB, int W>
 __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char* smem) {
@@ -148,6 +169,55 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     for (int db = 0; db < DB; ++db) T.vf[db] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (db * 16 + l16) * kBlockSize));
     T.kt = kt;
   };
+  // 8-wave kernels: the wave's LDS slot (K tile, then V tile) and the per-lane
+  // copy sources and operand read addresses. Piece c (16 bytes) of key k of the
+  // K tile sits at position c ^ kswz(k) of the key's row, so that the 16 keys
+  // one operand read touches fall in 16 different bank groups; the two 16-byte
+  // halves of a V row are swapped on bit 3 of the row for the same reason.
+  constexpr int NI = D / 16;           // 1 KB copies per K (and per V) tile
+  constexpr int KROW = D * 2;          // bytes of a K row
+  constexpr int NC = D / 8;            // 16-byte pieces of a K row
+  constexpr int KPI = 1024 / KROW;     // keys per K copy
+  constexpr int VBLK = kBlockSize * D * 2;  // bytes of one block's V head (and K head)
+  const uint32_t kslot = lds_addr(smem) + uint32_t(wave * 2 * NI * 1024);
+  const uint32_t vslot = kslot + uint32_t(NI * 1024);
+  uint32_t k_src[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int key = i * KPI + lane / NC;  // key of the tile this lane copies, < 32
+    k_src[i] = uint32_t((key % kBlockSize) * KROW + (((lane % NC) ^ kswz<D>(key)) << 4));
+  }
+  const uint32_t v_src0 = uint32_t((lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 4) & 1)) << 4));
+  const int key0 = 8 * (l16 >> 2) + (l16 & 3);  // key of MFMA row l16 in block 0
+  const uint32_t k_rd = kslot + uint32_t(key0 * KROW + ((q4 ^ kswz<D>(key0)) << 4));
+  const uint32_t v_rd = vslot + uint32_t((q4 >> 1) * VBLK + l16 * 32 + (((q4 & 1) ^ ((l16 >> 3) & 1)) << 4));
+  // Copy tile jj (K, then V) into the wave's slot: 2 NI direct copies of whole lines.
+  auto issue_tile = [&](int jj) {
+    const int e = (2 * (jj - tw0)) & (64 * IDR - 1);
+    const int32_t s0 = id_at(e), s1 = id_at(e + 1);
+    const uint16_t* k0 = blk_base(kc, s0);
+    const uint16_t* k1 = blk_base(kc, s1);
+    const uint16_t* v0 = blk_base(vc, s0);
+    const uint16_t* v1 = blk_base(vc, s1);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16_nt(i < NI / 2 ? k0 : k1, k_src[i], kslot + uint32_t(i * 1024));
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      dma16_nt(i < NI / 2 ? v0 : v1, v_src0 + uint32_t((i % (NI / 2)) * 1024), vslot + uint32_t(i * 1024));
+  };
+  // Operands of tile jj from the slot (its copies have landed).
+  auto read_tile = [&](Tile& T, int jj) {
+    typedef __attribute__((address_space(3))) const u32x4 lds_cq_t;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t ka = k_rd ^ uint32_t(ks << 6);  // piece 4 ks + q4: bits 6-7 of the row offset
+#pragma unroll
+      for (int b = 0; b < 2; ++b) T.kf[b][ks] = *reinterpret_cast<lds_cq_t*>(ka + uint32_t(b * 4 * KROW));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) T.vf[db] = *reinterpret_cast<lds_cq_t*>(v_rd + uint32_t(db * 16 * 32));
+    T.kt = it.key_begin + jj * kSplitTile;
+  };
   auto compute = [&](Tile& T) {
     const int kt = T.kt;
     u32x4 pf[RB];
@@ -236,25 +306,23 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
         load(jj + k + NT, tl[k]);
       }
     }
-  } else if constexpr (RB == 1) {
-    // Two tiles in flight. Loads are issued whether or not the tile is used (tiles
-    // past the wave's range read the zero page): a load under a branch would make
-    // the compiler wait for it where the branches join.
-    Tile ta, tb;
-    load(tw0, ta);
-    for (int jj = tw0; jj < tw1; jj += 2) {
-      load(jj + 1, tb);
-      compute(ta);
-      load(jj + 2, ta);
-      if (jj + 1 < tw1) compute(tb);
-    }
   } else {
-    Tile ta;
-    load(tw0, ta);
+    // Tile jj + 1 is copied into the slot while tile jj is computed from registers.
+    // The compiler sees none of these copies, so the two waits here are the only
+    // ones: every copy has landed before the slot is read, and the reads have
+    // returned before the slot is overwritten. The copy past the wave's range (any
+    // valid block id, or the zero page) is drained before the merge reuses the LDS.
+    issue_tile(tw0);
     for (int jj = tw0; jj < tw1; ++jj) {
-      compute(ta);
-      load(jj + 1, ta);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      Tile T;
+      read_tile(T, jj);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue_tile(jj + 1);
+      compute(T);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
   // Merge the waves' partial results through LDS (the page's merge rule over the
