@@ -231,22 +231,16 @@ int build_plan(int32_t num_seqs, const int32_t* prefix, const int32_t* extend, i
     // heads), each tile's key range is cut into pieces, one workgroup each, and the
     // combine kernel merges the pieces by the page's rule (the one-GPU share of a
     // context-parallel split of the prefix).
-    // Alone, the tiles take floor(target / tiles) pieces each, so that the pieces fill
-    // whole rounds of the CUs; next to split items, ceil(target / tiles), whose finer
-    // pieces interleave with the split items (measured: the mixed step's kernel span
-    // 0.394 ms against 0.427 with whole tiles, its chunk rows alone 0.245 ms against
-    // 0.257 with two pieces a tile).
+    // The tiles take floor(target / tiles) pieces each, so that the pieces fill whole
+    // rounds of the CUs, also next to split items (measured on the mixed step, whose
+    // 248 tiles then run whole: 0.385-0.390 ms a call against 0.393-0.398 with two
+    // pieces a tile and the combine of their partials, kernel span unchanged).
     int64_t chunk_tiles = 0;
-    bool any_split = false;
     for (int32_t r = 0; r < num_seqs; ++r) {
       const int64_t rows = int64_t(extend[r]) * group;
       if (rows > split_max_rows) chunk_tiles += (rows + kRowsPerTile - 1) / kRowsPerTile * hkv;
-      else any_split = true;
     }
-    const int64_t chunk_pieces =
-        chunk_tiles == 0 ? 1
-        : any_split      ? std::max<int64_t>(1, (kChunkTargetItems + chunk_tiles - 1) / chunk_tiles)
-                         : std::max<int64_t>(1, kChunkTargetItems / chunk_tiles);
+    const int64_t chunk_pieces = chunk_tiles == 0 ? 1 : std::max<int64_t>(1, kChunkTargetItems / chunk_tiles);
     for (int32_t r = 0; r < num_seqs; ++r) {
       const int64_t rows = int64_t(extend[r]) * group;
       const int64_t kv_len = int64_t(prefix[r]) + extend[r];

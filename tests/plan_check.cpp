@@ -12,7 +12,7 @@
 //  * keep split items within the per-wave id budget (kSplitKeysMax keys; kWideKeysMax
 //    on the 4-wave wide-split kernel) and the row limit of the kernel that runs them;
 //  * give a fused append min(items, kAppendProducers) copying workgroups;
-//  * in a launch of chunk rows only, cut tiles into whole rounds of key pieces;
+//  * cut chunk tiles into whole rounds of key pieces, with or without split items;
 //  * keep the tiles of one chunk group (request, KV head) on a contiguous run of die
 //    lanes (list positions modulo kXcds) while every lane still has items.
 // Exit status 0 when every launch passes; the first violation is printed.
@@ -136,20 +136,20 @@ static bool check_launch(const std::vector<int32_t>& P, const std::vector<int32_
     const int cnt = m == merged.end() ? 0 : m->second;
     CHECK(cnt == (split ? 1 : 0), "seed %u: row merged %d times (pieces %zu)", seed, cnt, kv.second.size());
   }
-  // 4b. a launch of chunk rows only cuts its tiles into whole rounds of pieces: no
-  //     more items than max(kChunkTargetItems, tiles) unless a few-row tile streams
-  //     its keys in split-length pieces
+  // 4b. chunk tiles are cut into whole rounds of pieces, next to split items too: no
+  //     more chunk items than max(kChunkTargetItems, tiles) unless a few-row tile
+  //     streams its keys in split-length pieces
   {
-    bool chunk_only = true, few = false;
+    bool few = false;
     int64_t tiles = 0, items = 0;
     for (int r = 0; r < n; ++r) {
       const int64_t rows = int64_t(E[r]) * G;
-      if (rows <= (plan.wide ? kWideMaxRows : kSplitMaxRows)) chunk_only = false;
+      if (rows <= (plan.wide ? kWideMaxRows : kSplitMaxRows)) continue;  // split rows
       tiles += (rows + kRowsPerTile - 1) / kRowsPerTile * hkv;
       if (rows % kRowsPerTile != 0 && rows % kRowsPerTile <= kFewRows) few = true;
     }
     for (size_t i = first; i < plan.items.size(); ++i) items += plan.items[i].kind == kItemChunk ? 1 : 0;
-    if (chunk_only && !few)
+    if (!few)
       CHECK(items <= std::max<int64_t>(kChunkTargetItems, tiles), "seed %u: %lld chunk items for %lld tiles", seed,
             (long long)items, (long long)tiles);
   }
