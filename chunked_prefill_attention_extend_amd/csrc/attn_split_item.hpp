@@ -326,7 +326,9 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   }
 
   // Merge the waves' partial results through LDS (the page's merge rule over the
-  // W parts): part[w][row][d] holds unnormalised o, mls[w][row] = (m, l).
+  // W parts): part[w][row][d] holds unnormalised o, mls[w][row] = (m, l). The 16-byte
+  // piece j of a row sits at j ^ (row % 16): the 16 rows a wave writes at once then
+  // fall in 16 different bank groups, and a row is still read whole.
   constexpr int SR = RB * kSplitRows;  // rows per wave and rows of the partial slot
   float* part = reinterpret_cast<float*>(smem);
   float* mls = part + W * SR * D;
@@ -338,7 +340,7 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     if (rr < it.nrows) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<float4*>(part + (wave * SR + rr) * D + db * 16 + 4 * q4) =
+        *reinterpret_cast<float4*>(part + (wave * SR + rr) * D + (((db * 4 + q4) ^ (rr & 15)) << 2)) =
             float4{o[rb][db][0], o[rb][db][1], o[rb][db][2], o[rb][db][3]};
       if (q4 == 0) {
         mls[(wave * SR + rr) * 2] = m[rb];
@@ -364,7 +366,7 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
         const float lw = mls[(w * SR + r) * 2 + 1];
         if (lw > 0.f) {
           const float f = __builtin_amdgcn_exp2f(mls[(w * SR + r) * 2] - M);
-          const float4 ow = *reinterpret_cast<const float4*>(part + (w * SR + r) * D + c4);
+          const float4 ow = *reinterpret_cast<const float4*>(part + (w * SR + r) * D + (((c4 >> 2) ^ (r & 15)) << 2));
           L += f * lw;
           acc.x += f * ow.x;
           acc.y += f * ow.y;
