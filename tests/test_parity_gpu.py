@@ -117,6 +117,23 @@ def test_verify_rows_40_to_64(d):
     assert torch.equal(out, o2) and torch.equal(lse, l2)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_split_tiles_through_lds(d):
+    """Decode and verify rows on the 8-wave kernel's split items (32 query / 8 KV
+    heads, 1..8 tokens: 4..32 rows per KV head, one and two 16-row blocks), whose
+    waves copy their K/V tiles into LDS slots and read them back in operand layout:
+    contexts from 1 key to several key pieces (merged by the combine kernel), ends at
+    and next to block (16), tile (32) and wave-round (256 keys) boundaries, waves
+    with no tile at all. Every row of every request against the oracle."""
+    ctx = [1, 13, 31, 32, 33, 255, 256, 257, 1000, 4099, 8191, 8193, 20000]
+    es = [1, 2, 4, 5, 8, 1, 3, 6, 7, 8, 1, 4, 2]
+    launches = [(L - e, e) for L, e in zip(ctx, es)]
+    w = custom_workload(91 + d, launches, 32, 8, d)
+    log(f"split tiles through LDS: {len(launches)} requests, contexts 1..20000, 32/8 heads, D={d}")
+    out, lse, q_off, q = run_launch(w)
+    check_launch(w, out, lse, q_off, q, what=f"split tiles through LDS, D={d}")
+
+
 def test_long_chunk_from_empty_prefix():
     """The largest chunk of the pages' workloads and then some: one 32768-token prompt
     from an empty cache (32 / 8 heads: 512 tiles per KV head, keys up to 32768),
