@@ -191,34 +191,46 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
   const int key0 = 8 * (l16 >> 2) + (l16 & 3);  // key of MFMA row l16 in block 0
   const uint32_t k_rd = kslot + uint32_t(key0 * KROW + ((q4 ^ kswz<D>(key0)) << 4));
   const uint32_t v_rd = vslot + uint32_t((q4 >> 1) * VBLK + l16 * 32 + (((q4 & 1) ^ ((l16 >> 3) & 1)) << 4));
-  // Copy tile jj (K, then V) into the wave's slot: 2 NI direct copies of whole lines.
-  auto issue_tile = [&](int jj) {
+  // Copy the K (or V) tile of tile jj into its half of the wave's slot: NI direct
+  // copies of whole lines.
+  auto issue_half = [&](int jj, bool v) {
     const int e = (2 * (jj - tw0)) & (64 * IDR - 1);
     const int32_t s0 = id_at(e), s1 = id_at(e + 1);
-    const uint16_t* k0 = blk_base(kc, s0);
-    const uint16_t* k1 = blk_base(kc, s1);
-    const uint16_t* v0 = blk_base(vc, s0);
-    const uint16_t* v1 = blk_base(vc, s1);
+    const uint16_t* c = v ? vc : kc;
+    const uint16_t* b0 = blk_base(c, s0);
+    const uint16_t* b1 = blk_base(c, s1);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16_nt(i < NI / 2 ? k0 : k1, k_src[i], kslot + uint32_t(i * 1024));
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      dma16_nt(i < NI / 2 ? v0 : v1, v_src0 + uint32_t((i % (NI / 2)) * 1024), vslot + uint32_t(i * 1024));
+    for (int i = 0; i < NI; ++i) {
+      if (v)
+        dma16_nt(i < NI / 2 ? b0 : b1, v_src0 + uint32_t((i % (NI / 2)) * 1024), vslot + uint32_t(i * 1024));
+      else
+        dma16_nt(i < NI / 2 ? b0 : b1, k_src[i], kslot + uint32_t(i * 1024));
+    }
   };
-  // Operands of tile jj from the slot (its copies have landed).
-  auto read_tile = [&](Tile& T, int jj) {
-    typedef __attribute__((address_space(3))) const u32x4 lds_cq_t;
+  typedef __attribute__((address_space(3))) const u32x4 lds_cq_t;
+  // K operands of tile jj from the slot (its K copies have landed).
+  auto read_k = [&](Tile& T, int jj) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint32_t ka = k_rd ^ uint32_t(ks << 6);  // piece 4 ks + q4: bits 6-7 of the row offset
 #pragma unroll
       for (int b = 0; b < 2; ++b) T.kf[b][ks] = *reinterpret_cast<lds_cq_t*>(ka + uint32_t(b * 4 * KROW));
     }
-#pragma unroll
-    for (int db = 0; db < DB; ++db) T.vf[db] = *reinterpret_cast<lds_cq_t*>(v_rd + uint32_t(db * 16 * 32));
     T.kt = it.key_begin + jj * kSplitTile;
   };
-  auto compute = [&](Tile& T) {
+  // V operands of tile jj, once its V copies have landed (only the next tile's K
+  // copies, issued after them, may still be in flight), then the next tile's V copies
+  // into the freed half. Runs between a tile's weights and its P.V products.
+  auto fetch_v = [&](Tile& T, int jj) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+#pragma unroll
+    for (int db = 0; db < DB; ++db) T.vf[db] = *reinterpret_cast<lds_cq_t*>(v_rd + uint32_t(db * 16 * 32));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue_half(jj + 1, true);
+  };
+  // before_pv(T) runs between the weights and the P.V products (fetch_v on the
+  // 8-wave kernel, nothing on the register ring of the wide kernel).
+  auto compute = [&](Tile& T, auto&& before_pv) {
     const int kt = T.kt;
     u32x4 pf[RB];
     // With Q in LDS, a block's KS operand pieces are read together, once per tile,
@@ -283,6 +295,7 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
         pf[rb][2 * b + 1] = pack2(p2, p3);
       }
     }
+    before_pv(T);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const u32x4 vv = clip_keys(T.vf[db], kt + 8 * q4, kv_len);
@@ -302,24 +315,29 @@ __device__ void split_item(const AttnArgs& a, const WorkItem& it, unsigned char*
     for (int jj = tw0; jj < tw1; jj += NT) {
 #pragma unroll
       for (int k = 0; k < NT; ++k) {
-        if (k == 0 || jj + k < tw1) compute(tl[k]);
+        if (k == 0 || jj + k < tw1) compute(tl[k], [](Tile&) {});
         load(jj + k + NT, tl[k]);
       }
     }
   } else {
-    // Tile jj + 1 is copied into the slot while tile jj is computed from registers.
-    // The compiler sees none of these copies, so the two waits here are the only
-    // ones: every copy has landed before the slot is read, and the reads have
-    // returned before the slot is overwritten. The copy past the wave's range (any
-    // valid block id, or the zero page) is drained before the merge reuses the LDS.
-    issue_tile(tw0);
+    // Tile jj + 1 is copied into the slot while tile jj is computed from registers,
+    // each half as soon as tile jj's operands have left it: K after its reads at the
+    // start of the tile, V after its reads before the P.V products. The copies go
+    // out in the order K(jj), V(jj), K(jj + 1), V(jj + 1), so each wait leaves
+    // exactly the later half's NI copies in flight. The compiler sees none of these
+    // copies, so these waits are the only ones: every copy has landed before its half
+    // is read, and the reads have returned before the half is overwritten. The
+    // copies past the wave's range (any valid block id, or the zero page) are
+    // drained before the merge reuses the LDS.
+    issue_half(tw0, false);
+    issue_half(tw0, true);
     for (int jj = tw0; jj < tw1; ++jj) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
       Tile T;
-      read_tile(T, jj);
+      read_k(T, jj);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue_tile(jj + 1);
-      compute(T);
+      issue_half(jj + 1, false);
+      compute(T, [&](Tile& t) { fetch_v(t, jj); });
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
